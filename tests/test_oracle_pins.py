@@ -1,0 +1,491 @@
+"""Pins of the CPU oracle to facts other than itself (no GPU needed).
+
+Sources: the vLLM API page vllm.models.kimi_k3.nvidia.specialized_decode.
+cutedsl.kda.wide (class KdaWide: docstring, constructor, kernel body, helpers
+silu and decay).  The page prints no worked example, so the pins are
+invariants, closed forms, special cases and an independent float64 matrix
+formulation.  Which step each pin covers:
+
+  slot resolution, padding ............ test_padding_*, test_contract_errors
+  convolution (tap order, window) ..... test_conv_tap_selection, test_conv_window_update
+  SiLU stage .......................... test_silu_textbook
+  L2 norm, q/k roles, o = S^T q ....... test_zero_state_closed_form, test_delta_rule_*
+  gate projection (indexing) .......... test_gate_one_hot
+  decay (formula, per-key axis) ....... test_decay_golden, test_decay_through_state
+  beta = sigmoid(logit) ............... test_identity_invariant, test_zero_state_closed_form
+  recurrence order and orientation .... test_delta_rule_*, test_zero_state_closed_form
+  verify slots / per-token writes ..... test_verify_equals_chained_decode
+  record outputs ...................... test_record_replay
+  gated RMSNorm ....................... test_rmsnorm_closed_form, test_zero_state_closed_form
+  everything together ................. test_matrix_form_cross_check
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+from linear_attention_decode_03_amd import inputs
+from linear_attention_decode_03_amd.inputs import from_bf16, to_bf16
+
+from . import _matrix_form
+
+D = 128
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LOGIT_ONE = 30.0     # sigmoid(30) rounds to 1.0 in FP32
+LOGIT_ZERO = -200.0  # sigmoid(-200) rounds to 0.0 in FP32
+
+
+def small(T=1, B=3, H=2, seed=11, **kw):
+    if T == 1:
+        cfg = dict(B=B, H=H, T=1, N=2 * B + 2, W=3, seed=seed)
+    else:
+        cfg = dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=seed)
+    cfg.update(kw)
+    return inputs.make_problem(cfg)
+
+
+def read_slot(p, b):
+    return int(p["slots"][b]) if p["T"] == 1 else int(p["slots"][b, p["accepted"][b] - 1])
+
+
+def bf16_of_f64(x):
+    """FP32 value of a float64, then BF16 (the page's rounding points)."""
+    return from_bf16(to_bf16(np.asarray(x, dtype=np.float64).astype(np.float32)))
+
+
+def silu64(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def set_conv_taps(p, part, taps):
+    """Sets the 4 convolution weights of one part (0 q, 1 k, 2 v) for every channel."""
+    p["conv_w"][part] = to_bf16(np.asarray(taps, dtype=np.float32))[:, None]
+
+
+# --------------------------------------------------------------------------
+# contract and padding
+
+
+def test_contract_errors(oracle_lib):
+    p = small()
+    for T, rec, gm in ((0, 0, 0), (9, 0, 0), (1, 0, 2), (1, 1, 0)):
+        q = inputs.copy_problem(p)
+        q["T"], q["record"], q["gate_mode"] = T, rec, gm
+        with pytest.raises(ValueError):
+            oracle_lib.run(q)
+
+
+def test_padding_leaves_everything_but_zero_output(oracle_lib):
+    p = small(B=5)
+    p["slots"][1] = 0
+    p["slots"][3] = -7
+    before = inputs.copy_problem(p)
+    oracle_lib.run(p)
+    for b in (1, 3):
+        assert np.all(p["out"][b] == 0)  # +0 in BF16, bit-exact
+    for b in (0, 2, 4):
+        assert not np.any(p["out"][b] == inputs.BF16_SENTINEL)
+        s = int(p["slots"][b])
+        assert not np.array_equal(p["state"][s], before["state"][s])
+    live = {int(p["slots"][b]) for b in (0, 2, 4)}
+    for s in range(p["N"]):
+        if s not in live:
+            assert np.array_equal(p["state"][s], before["state"][s])
+            assert np.array_equal(p["conv_state"][s], before["conv_state"][s])
+
+
+def test_padding_verify_per_token_target(oracle_lib):
+    """A verify target <= 0 skips only that token's state write."""
+    p = small(T=3, B=2)
+    p["accepted"][:] = 1
+    skipped = int(p["slots"][0, 1])
+    p["slots"][0, 1] = 0
+    before = inputs.copy_problem(p)
+    oracle_lib.run(p)
+    assert np.array_equal(p["state"][skipped], before["state"][skipped])
+    assert np.array_equal(p["state"][0], before["state"][0])
+    for t in (0, 2):
+        s = int(p["slots"][0, t])
+        assert not np.array_equal(p["state"][s], before["state"][s])
+
+
+# --------------------------------------------------------------------------
+# invariant (1): decay = 1 and beta = 0 leave the state unchanged
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_identity_invariant(oracle_lib, T):
+    p = small(T=T, lower_bound=0.0)
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, LOGIT_ZERO, np.float32))
+    before = inputs.copy_problem(p)
+    oracle_lib.run(p)
+    for b in range(p["B"]):
+        src = before["state"][read_slot(before, b)]
+        targets = [int(p["slots"][b])] if T == 1 else [int(s) for s in p["slots"][b, :T]]
+        for tgt in targets:
+            assert np.array_equal(p["state"][tgt].view(np.uint32), src.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# invariant (2) and the textbook delta-rule recall
+
+
+def test_delta_rule_beta_one(oracle_lib):
+    """beta = 1: after the update S^T k_hat = v for every value row."""
+    p = small(B=4)
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, LOGIT_ONE, np.float32))
+    taps = oracle_lib.run(p, taps=True)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            S = p["state"][int(p["slots"][b]), h].astype(np.float64)  # [v][k]
+            k = taps["k"][b, h, 0].astype(np.float64)
+            kh = k / np.sqrt((k * k).sum() + 1e-6)
+            v = taps["v"][b, h, 0].astype(np.float64)
+            u = taps["u"][b, h, 0].astype(np.float64)
+            lhs = S @ kh
+            assert np.all(np.abs(lhs - v) <= 1e-5 * (np.abs(v) + np.abs(u) + 1e-3))
+
+
+def test_delta_rule_recall_one_hot_keys(oracle_lib):
+    """Associative-memory recall: with no decay (lb = 0), beta = 1 and
+    orthonormal keys e_{j_t}, after T tokens S^T e_{j_t} = v_t for every t."""
+    T = 4
+    p = small(T=T, B=2, H=2, lower_bound=0.0)
+    p["accepted"][:] = 1
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, LOGIT_ONE, np.float32))
+    set_conv_taps(p, 1, [0, 0, 0, 1])  # k_t = silu(x_k,t)
+    set_conv_taps(p, 2, [0, 0, 0, 1])  # v_t = silu(x_v,t)
+    dim = p["H"] * D
+    keys = [5, 77, 31, 120]
+    for b in range(p["B"]):
+        for t in range(T):
+            row = p["x"][b * T + t]
+            row[dim:2 * dim] = 0
+            for h in range(p["H"]):
+                row[dim + h * D + keys[t]] = to_bf16(np.float32(3.0)).item()
+    before = inputs.copy_problem(p)
+    oracle_lib.run(p)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            S = p["state"][int(p["slots"][b, T - 1]), h].astype(np.float64)  # [v][k]
+            for t in range(T):
+                xv = from_bf16(before["x"][b * T + t, 2 * dim + h * D:2 * dim + (h + 1) * D])
+                v_t = bf16_of_f64(silu64(xv)).astype(np.float64)
+                col = S[:, keys[t]]
+                # k_hat_j = s / sqrt(s^2 + 1e-6), 1 - k_hat_j ~ 6e-8
+                assert np.allclose(col, v_t, rtol=2e-6, atol=1e-7)
+
+
+# --------------------------------------------------------------------------
+# invariant (3): a T-token verify equals T chained single-token decodes
+
+
+@pytest.mark.parametrize("T", [2, 4, 8])
+def test_verify_equals_chained_decode(oracle_lib, T):
+    p = small(T=T, B=3, H=2, seed=20 + T)
+    p["accepted"][:] = 1
+    B, H = p["B"], p["H"]
+    dim = H * D
+    chain = dict(p)
+    chain.update(T=1, W=3, slot_stride=1, record=0, accepted=None, rec_u=None, rec_kg=None)
+    chain["slots"] = np.ascontiguousarray(p["slots"][:, 0])
+    chain["state"] = p["state"].copy()
+    chain["conv_state"] = np.ascontiguousarray(p["conv_state"][:, :, :3])
+    outs = []
+    states = []
+    for t in range(T):
+        rows = np.arange(B) * T + t
+        step = dict(chain)
+        for key in ("x", "f_a", "beta", "gate"):
+            step[key] = np.ascontiguousarray(p[key][rows])
+        step["out"] = np.zeros((B, dim), np.uint16)
+        oracle_lib.run(step)
+        outs.append(step["out"])
+        states.append({b: chain["state"][int(chain["slots"][b])].copy() for b in range(B)})
+    conv_before = p["conv_state"].copy()
+    oracle_lib.run(p)
+    for t in range(T):
+        assert np.array_equal(p["out"][np.arange(B) * T + t], outs[t])
+        for b in range(B):
+            got = p["state"][int(p["slots"][b, t])]
+            assert np.array_equal(got.view(np.uint32), states[t][b].view(np.uint32))
+    for b in range(B):
+        cs = int(p["slots"][b, 0])
+        assert np.array_equal(p["conv_state"][cs][:, T - 1:T + 2], chain["conv_state"][cs])
+    assert conv_before.shape == p["conv_state"].shape
+
+
+# --------------------------------------------------------------------------
+# (5) the decay formula
+
+
+def test_decay_golden(oracle_lib):
+    rows = [line.split() for line in open(os.path.join(GOLDEN, "decay_special_values.txt"))
+            if line.strip() and not line.startswith("#")]
+    assert len(rows) >= 10
+    for a_log, g, dt, lb, hexv in rows:
+        got = np.float32(oracle_lib.decay(float(a_log), float(g), float(dt), float(lb)))
+        assert got.view(np.uint32) == np.uint32(int(hexv, 16)), (a_log, g, dt, lb)
+
+
+def test_decay_through_state(oracle_lib):
+    """State all ones and beta = 0: the new state holds the decay, identical
+    for every value row and varying along the key axis.  F_B rows are one-hot
+    through a permutation with no fixed points, so raw_g[f] = f_a[pi(f)]."""
+    p = small(B=2, H=2)
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, LOGIT_ZERO, np.float32))
+    p["state"][:] = 1.0
+    pi = (np.arange(D) * 37 + 11) % D
+    fb = np.zeros((p["H"] * D, D), np.float32)
+    for h in range(p["H"]):
+        fb[h * D + np.arange(D), pi] = 1.0
+    p["f_b"] = to_bf16(fb)
+    oracle_lib.run(p)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            S = p["state"][int(p["slots"][b]), h]
+            assert np.all(S == S[0:1, :])          # every value row identical
+            fa = from_bf16(p["f_a"][b]).astype(np.float64)
+            z = fa[pi] + p["dt_bias"][h * D:(h + 1) * D].astype(np.float64)
+            lb = p["lower_bound"]
+            y = math.exp(float(p["a_log"][h])) * z
+            sig = 1.0 / (1.0 + np.exp(-y))
+            a = np.exp(lb * sig)
+            # FP32 rounding bound of the five-step chain z, e, y, sigma, g, exp
+            # (unit roundoff u): |dy| <= 3u|y|, |ds| <= s(1-s)|dy| + u s,
+            # |dg| <= |lb||ds| + u|lb s|, |da|/a <= |dg| + u.
+            u = 2.0 ** -24
+            ds = sig * (1 - sig) * 3 * u * np.abs(y) + u * sig
+            bound = a * (abs(lb) * ds + u * abs(lb) * sig + u)
+            assert np.all(np.abs(S[0].astype(np.float64) - a) <= 1.5 * bound + 1e-300)
+
+
+# --------------------------------------------------------------------------
+# convolution, SiLU and gate special cases
+
+
+def test_silu_textbook(oracle_lib):
+    xs = np.concatenate([np.linspace(-12, 12, 2001), [-100.0, -88.0, 0.0, 1e-3, 50.0]])
+    xs = from_bf16(to_bf16(xs.astype(np.float32)))  # BF16-exact inputs, as the conv sees
+    for x in xs:
+        got = oracle_lib.silu_bf16(float(x))
+        want = float(bf16_of_f64(silu64(float(x)))[()])
+        assert got == want or (math.isnan(got) and math.isnan(want)), x
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_conv_tap_selection(oracle_lib, T):
+    """One-hot tap weights select one window entry: weight i selects
+    window[t + i] of [conv[off], conv[off+1], conv[off+2], x_0, ..., x_{T-1}]."""
+    p = small(T=T, B=2, H=2)
+    if T > 1:
+        p["accepted"][:] = [2, 3]
+    dim = p["H"] * D
+    for tap in range(4):
+        q = inputs.copy_problem(p)
+        for part in range(3):
+            w = [0.0] * 4
+            w[tap] = 1.0
+            set_conv_taps(q, part, w)
+        taps = oracle_lib.run(q, taps=True)
+        for b in range(p["B"]):
+            off = 0 if T == 1 else int(p["accepted"][b]) - 1
+            cs = int(p["slots"][b]) if T == 1 else int(p["slots"][b, 0])
+            for h in range(p["H"]):
+                for part, name in enumerate(("q", "k", "v")):
+                    ch = part * dim + h * D + np.arange(D)
+                    window = [from_bf16(p["conv_state"][cs][ch, off + i]) for i in range(3)]
+                    window += [from_bf16(p["x"][b * T + t, ch]) for t in range(T)]
+                    for t in range(T):
+                        want = bf16_of_f64(silu64(window[t + tap]))
+                        assert np.array_equal(taps[name][b, h, t], want)
+
+
+def test_conv_window_update(oracle_lib):
+    """Window after the step: [tap1, tap2, x_0, ..., x_{T-1}], bits copied."""
+    for T in (1, 3):
+        p = small(T=T, B=2, H=1)
+        if T > 1:
+            p["accepted"][:] = [3, 2]
+        before = inputs.copy_problem(p)
+        oracle_lib.run(p)
+        dim = D
+        for b in range(2):
+            off = 0 if T == 1 else int(p["accepted"][b]) - 1
+            cs = int(p["slots"][b]) if T == 1 else int(p["slots"][b, 0])
+            old = before["conv_state"][cs]
+            new = p["conv_state"][cs]
+            assert np.array_equal(new[:, 0], old[:, off + 1])
+            assert np.array_equal(new[:, 1], old[:, off + 2])
+            for t in range(T):
+                assert np.array_equal(new[:, 2 + t], before["x"][b * T + t, :3 * dim])
+            assert np.array_equal(new[:, 2 + T:], old[:, 2 + T:])
+
+
+def test_gate_one_hot(oracle_lib):
+    """One-hot F_B rows: raw_g[f] = f_a[pi(f)] bit for bit (record output)."""
+    T = 2
+    p = small(T=T, B=2, H=2, record=1)
+    pi = (np.arange(D) * 53 + 7) % D
+    fb = np.zeros((p["H"] * D, D), np.float32)
+    for h in range(p["H"]):
+        fb[h * D + np.arange(D), (pi + h) % D] = 1.0
+    p["f_b"] = to_bf16(fb)
+    oracle_lib.run(p)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            for t in range(T):
+                want = p["f_a"][b * T + t][(pi + h) % D]
+                assert np.array_equal(p["rec_kg"][b, h, t, D:], want)
+
+
+# --------------------------------------------------------------------------
+# closed forms through the whole step
+
+
+def test_zero_state_closed_form(oracle_lib):
+    """S = 0 and q = k: S_new = k_hat u^T with u = v * beta, and
+    o_v = u_v * (k_hat . q_hat) = u_v * scale * |k_hat|^2; the output is the
+    gated RMSNorm of that o."""
+    p = small(B=3, H=2, seed=31)
+    p["state"][:] = 0.0
+    dim = p["H"] * D
+    p["conv_w"][0] = p["conv_w"][1]
+    p["x"][:, :dim] = p["x"][:, dim:2 * dim]
+    p["conv_state"][:, :dim] = p["conv_state"][:, dim:2 * dim]
+    taps = oracle_lib.run(p, taps=True)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            k = taps["k"][b, h, 0].astype(np.float64)
+            v = taps["v"][b, h, 0].astype(np.float64)
+            beta = 1.0 / (1.0 + np.exp(-float(from_bf16(p["beta"][b, h])[()])))
+            kh = k / np.sqrt((k * k).sum() + 1e-6)
+            S = p["state"][int(p["slots"][b]), h].astype(np.float64)
+            assert np.allclose(S, np.outer(v * beta, kh), rtol=1e-6, atol=1e-9)
+            o = v * beta * p["scale"] * (kh * kh).sum()
+            assert np.allclose(taps["o_exact"][b, h, 0], o, rtol=1e-5, atol=1e-9)
+            o_bf = bf16_of_f64(o).astype(np.float64)
+            g = from_bf16(p["gate"][b, h * D:(h + 1) * D]).astype(np.float64)
+            nw = from_bf16(p["norm_w"]).astype(np.float64)
+            want = o_bf / np.sqrt((o_bf ** 2).mean() + p["eps"]) * nw / (1 + np.exp(-g))
+            got = from_bf16(p["out"][b, h * D:(h + 1) * D]).astype(np.float64)
+            assert np.all(np.abs(got - want) <= 2 * 2.0 ** (np.floor(np.log2(np.abs(want) + 1e-30)) - 7))
+
+
+def test_norm_epsilon_small_keys(oracle_lib):
+    """The 1e-6 of the L2 norm is added to the sum of squares: with q = k of
+    sum of squares m ~ 1e-6, zero state and beta = 1, S_new = v k_hat^T and
+    o = v * scale * m / (m + 1e-6)."""
+    p = small(B=2, H=2, seed=33)
+    p["state"][:] = 0.0
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, LOGIT_ONE, np.float32))
+    dim = p["H"] * D
+    for part in (0, 1):
+        set_conv_taps(p, part, [0, 0, 0, 1])
+    small_x = to_bf16(from_bf16(p["x"][:, dim:2 * dim]) * np.float32(2e-4))
+    p["x"][:, :dim] = small_x
+    p["x"][:, dim:2 * dim] = small_x
+    taps = oracle_lib.run(p, taps=True)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            k = taps["k"][b, h, 0].astype(np.float64)
+            v = taps["v"][b, h, 0].astype(np.float64)
+            m = (k * k).sum()
+            assert 1e-7 < m < 1e-5
+            kh = k / np.sqrt(m + 1e-6)
+            S = p["state"][int(p["slots"][b]), h].astype(np.float64)
+            assert np.allclose(S, np.outer(v, kh), rtol=1e-5, atol=1e-12)
+            o = v * p["scale"] * m / (m + 1e-6)
+            assert np.allclose(taps["o_exact"][b, h, 0], o, rtol=1e-5, atol=1e-12)
+
+
+def test_rmsnorm_closed_form(oracle_lib):
+    rng = np.random.default_rng(3)
+    o = from_bf16(to_bf16(rng.standard_normal(D).astype(np.float32)))
+    one = to_bf16(np.ones(D, np.float32))
+    sig1 = to_bf16(np.full(D, LOGIT_ONE, np.float32))
+    # eps = 0, nw = 1, gate sigma = 1: out = o / rms(o), so rms(out) = 1
+    out = from_bf16(oracle_lib.gated_rmsnorm(o, sig1, one, 0.0)).astype(np.float64)
+    assert abs(math.sqrt((out ** 2).mean()) - 1.0) < 2 ** -8
+    assert np.all(np.sign(out) == np.sign(o))
+    # eps = m: rms(out) = sqrt(m / (m + eps)) = sqrt(1/2)
+    m = float((o.astype(np.float64) ** 2).mean())
+    out = from_bf16(oracle_lib.gated_rmsnorm(o, sig1, one, m)).astype(np.float64)
+    assert abs(math.sqrt((out ** 2).mean()) - math.sqrt(0.5)) < 2 ** -8
+    # nw = 2 doubles the output exactly; a gate logit of -200 zeroes a channel
+    two = to_bf16(np.full(D, 2.0, np.float32))
+    base = from_bf16(oracle_lib.gated_rmsnorm(o, sig1, one, 1e-6))
+    dbl = from_bf16(oracle_lib.gated_rmsnorm(o, sig1, two, 1e-6))
+    assert np.array_equal(dbl, 2 * base)
+    gz = sig1.copy()
+    gz[[3, 64, 127]] = to_bf16(np.float32(LOGIT_ZERO))
+    zed = from_bf16(oracle_lib.gated_rmsnorm(o, gz, one, 1e-6))
+    assert np.all(zed[[3, 64, 127]] == 0) and np.array_equal(np.delete(zed, [3, 64, 127]),
+                                                             np.delete(base, [3, 64, 127]))
+
+
+# --------------------------------------------------------------------------
+# record mode (RecoverSSM): same outputs, no state write, replayable records
+
+
+def test_record_replay(oracle_lib):
+    T = 4
+    p = small(T=T, B=3, H=2, record=1, seed=41)
+    plain = inputs.copy_problem(p)
+    plain.update(record=0, rec_u=None, rec_kg=None)
+    before_state = p["state"].copy()
+    oracle_lib.run(p)
+    oracle_lib.run(plain)
+    assert np.array_equal(p["out"], plain["out"])
+    assert np.array_equal(p["conv_state"], plain["conv_state"])
+    assert np.array_equal(p["state"].view(np.uint32), before_state.view(np.uint32))  # no writes
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            S = before_state[read_slot(p, b), h].astype(np.float64)   # the checkpoint
+            dt = p["dt_bias"][h * D:(h + 1) * D]
+            for t in range(T):
+                k = from_bf16(p["rec_kg"][b, h, t, :D]).astype(np.float64)
+                g = from_bf16(p["rec_kg"][b, h, t, D:])
+                u = p["rec_u"][b, h, t].astype(np.float64)
+                a = np.array([oracle_lib.decay(float(p["a_log"][h]), float(g[f]), float(dt[f]),
+                                               p["lower_bound"]) for f in range(D)])
+                kh = k / np.sqrt((k * k).sum() + 1e-6)
+                S = S * a[None, :] + np.outer(u, kh)
+                ref = plain["state"][int(plain["slots"][b, t]), h].astype(np.float64)
+                rms = math.sqrt((ref ** 2).mean())
+                assert np.all(np.abs(S - ref) <= 1e-5 * (np.abs(ref) + rms))
+
+
+# --------------------------------------------------------------------------
+# the whole step against an independent float64 matrix formulation
+
+
+@pytest.mark.parametrize("name,T", [("tiny_decode", 1), ("small_verify", 4), ("small_verify8", 8)])
+def test_matrix_form_cross_check(oracle_lib, name, T):
+    """Where a BF16 rounding input sits within FP32 noise of a midpoint the two
+    formulations may round differently (the page fixes FP32 operations, the
+    matrix form is float64); there the matrix form takes the oracle's
+    neighbour, and such points must stay rare."""
+    if name == "tiny_decode":
+        p = inputs.make_problem("tiny_decode")
+    else:
+        p = small(T=T, B=2, H=2, seed=50 + T)
+    before = inputs.copy_problem(p)
+    taps = oracle_lib.run(p, taps=True)
+    ties = [0]
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            out, states = _matrix_form.step(before, b, h, taps=taps, counter=ties)
+            got = from_bf16(p["out"][b * T:(b + 1) * T, h * D:(h + 1) * D]).astype(np.float64)
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(out), 1e-30))) - 7)
+            assert np.all(np.abs(got - out) <= 2 * ulp)
+            for t in range(T):
+                tgt = int(p["slots"][b]) if T == 1 else int(p["slots"][b, t])
+                ref = states[t].T  # back to [value row][key]
+                g = p["state"][tgt, h].astype(np.float64)
+                rms = math.sqrt((ref ** 2).mean())
+                assert np.all(np.abs(g - ref) <= 1e-5 * (np.abs(ref) + rms))
+    assert ties[0] <= 0.05 * p["B"] * p["H"] * T * 5 * D
