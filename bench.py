@@ -1,0 +1,201 @@
+"""Throughput of the KDA decode step on one MI355X.
+
+One step = one launch of the whole hot path (slot resolution, convolution,
+gate projection, decay, L2 norm, recurrence, state write-back, window update,
+gated RMSNorm) over one batch: the decode workload B=256 requests x H=32
+heads (8192 items), T=1, d=128, a pool of 512 state slots (1 GiB FP32), with
+seeded synthetic inputs resident in HBM before the timed region.
+
+Prints one JSON line.  `value` is (request, head) items per second;
+`roofline` relates the kernel's algorithmic bytes per launch to its average
+duration, measured with HIP events around each launch on the launch stream;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --mode copy      # 1 GiB device copies (counter calibration)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "kda_decode_b256_pmc.txt")
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_03_amd", "csrc", "kda.hip")
+D = 128
+
+
+def algorithmic_bytes(p) -> int:
+    """Bytes the method must move for one launch (each operand once):
+    per live item: the 64 KiB state page read, 64 KiB written per stored
+    token (1 for decode, T for verify, 0 for record), records T KiB, the
+    3 read taps and T+2 written columns of its 384 convolution channels,
+    x (768 B), gate (256 B), beta (2 B) and out (256 B) per token; per padded
+    item its 256 B of zeros per token; per live request f_a (256 B per
+    token); the slot tables; once per launch the weights (F_B, conv weights,
+    dt_bias, A_log, norm weight)."""
+    import numpy as np
+
+    from linear_attention_decode_03_amd.inputs import live_items
+
+    B, H, T = p["B"], p["H"], p["T"]
+    live = len(live_items(p))
+    live_req = live // H
+    pad = B * H - live
+    stored = 0 if p["record"] else (1 if T == 1 else T)
+    per_live = (65536 * (1 + stored) + (1024 * T if p["record"] else 0)
+                + 3 * D * 3 * 2 + 3 * D * (T + 2) * 2 + T * (768 + 256 + 2 + 256))
+    total = live * per_live + pad * 256 * T + live_req * 256 * T
+    total += int(np.asarray(p["slots"]).nbytes) + (B * 4 if T > 1 else 0)
+    total += H * (3 * 4 * D * 2 + D * D * 2 + D * 4 + 4) + D * 2
+    return int(total)
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    fields = {}
+    for line in open(PROFILE_PMC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, min_seconds=10.0):
+    """The oracle as it is (single-threaded C) on the same workload: whole
+    passes over all items until at least `min_seconds` have elapsed."""
+    import oracle
+    from linear_attention_decode_03_amd.inputs import copy_problem
+
+    oracle.build(force=False)
+    q = copy_problem(p)
+    n_items = p["B"] * p["H"]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run(q)
+        done += n_items
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": done / el, "unit": "items/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done // n_items} full pass(es) over the {n_items} items of the "
+                      f"same workload, single-threaded, {el:.1f} s"}
+
+
+def run_copy(args):
+    import torch
+
+    n = 1 << 28  # 1 GiB of float32
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"mode": "copy", "bytes_per_copy": 2 * n * 4, "steps": args.steps,
+                      "gbps": 2 * n * 4 * args.steps / el / 1e9}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b256")
+    ap.add_argument("--ahead", type=int, default=-1)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", choices=["kda", "copy"], default="kda")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA step has no cross-GPU exchange and "
+              "this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.mode == "copy":
+        return run_copy(args)
+
+    from linear_attention_decode_03_amd import inputs, kda
+    from tests import _gpu
+
+    kda.load_library()
+    p = inputs.make_problem(args.workload)
+    print(f"[bench] workload {args.workload}: inputs ready", file=sys.stderr, flush=True)
+    d = _gpu.to_device(p)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        _gpu.run(d, ahead=args.ahead)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record()
+        _gpu.run(d, ahead=args.ahead)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durations_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1e3 / K
+    kernel_ms = sum(durations_ms) / K
+    print(f"[bench] {K} steps, {ms_per_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    items = p["B"] * p["H"]
+    abytes = algorithmic_bytes(p)
+    achieved = abytes / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": "KDA decode (request,head)-steps/sec and achieved HBM GB/s (% of peak)",
+        "value": items / (ms_per_step * 1e-3),
+        "unit": "items/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: KDA step T={p['T']}, B={p['B']} requests, "
+                               f"H={p['H']} heads, d=128, {p['N']}-slot FP32 state pool",
+                   "B": p["B"], "H": p["H"], "T": p["T"], "N": p["N"], "items": items,
+                   "record": p["record"], "gate_mode": p["gate_mode"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": abytes,
+                     "kernel_us": kernel_ms * 1e3},
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention decode / verify step.
+ *
+ * The operation is the one the vLLM API page
+ * vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.wide (class KdaWide)
+ * defines: for every (request b, head h) item, read the item's 128x128 FP32
+ * recurrent state from a slot-indexed pool and advance it through T tokens
+ * (T = 1: decode; T in [2, 8]: speculative verify).  Per token:
+ *   - a 4-tap causal convolution over the q, k and v channels against the
+ *     per-slot convolution window, then SiLU, rounded to BF16;
+ *   - q and k L2-normalised (1e-6 added to the sum of squares), q scaled;
+ *   - the gate projection raw_g = BF16(F_B[h] . f_a) and the per-key-channel
+ *     decay a = exp(lower_bound * sigmoid(exp(A_log[h]) * (raw_g + dt_bias)));
+ *   - beta = sigmoid(beta logit);
+ *   - the gated delta rule on the state S[v][k] (value row v, key k):
+ *       S <- S (.) a (along keys);  u_v = beta (v_v - S_v . k_hat);
+ *       S_v <- S_v + u_v k_hat;    o_v = S_v . q_hat, rounded to BF16;
+ *   - a gated RMSNorm: out = BF16(((o * rstd) * norm_w) * sigmoid(gate)),
+ *     rstd = (sum(o^2) / 128 + eps)^-1/2.
+ * The convolution window is rewritten to [tap1, tap2, x_0, ..., x_{T-1}].
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a DEVICE pointer owned by the caller; BF16 operands are
+ *     passed as uint16_t bit patterns.  All tensors are contiguous, row-major,
+ *     in the layouts given below.  The library allocates nothing, keeps no
+ *     state between calls and never synchronises.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  The call
+ *     validates its arguments on the host, then enqueues one kernel on
+ *     `stream` and returns; buffers must stay alive until the stream passes.
+ *   - `state` and `conv_state` are updated in place; `out`, `rec_u` and
+ *     `rec_kg` are written; everything else is read only.  `out`, `rec_u`
+ *     and `rec_kg` must not alias any input.
+ *   - Errors: on any non-OK status nothing is enqueued, except KDA_ERR_LAUNCH
+ *     (the launch itself failed).  B = 0 is a successful no-op.
+ *   - Caller contract, not checked on the device: the live read slots and
+ *     write targets are pairwise distinct across requests (a request may read
+ *     and write the same slot), and each live request's convolution slot is
+ *     its own.  Tables that break the range rules below never make the kernel
+ *     touch memory outside the pools: such an item is treated as padding.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128   /* dk = dv = 128 */
+#define KDA_CONV_TAPS 4
+#define KDA_MAX_TOKENS 8
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_TOKENS = 1,     /* T outside [1, 8] (the page's ValueError) */
+  KDA_ERR_GATE_MODE = 2,  /* gate_mode not 0 or 1 (the page's assertion) */
+  KDA_ERR_RECORD_T1 = 3,  /* record with T = 1 (the page's assertion) */
+  KDA_ERR_NULL = 4,       /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 5,      /* B < 0, H < 1, N < 1, W too small, slot_stride < T,
+                             non-finite scalar, or sizes beyond 32-bit grids */
+  KDA_ERR_LAUNCH = 6      /* the kernel launch failed (hipGetLastError) */
+} kda_status;
+
+/*
+ * kda_decode -- one decode step, T = 1 (KdaWide with tokens = 1).
+ *
+ * Slot resolution (the kernel body's first lines on the page): for request b,
+ * slot = slots[b] is both the state slot and the convolution slot; slot <= 0
+ * marks padding: the H*128 output values of the request are set to BF16 +0
+ * and nothing else is read or written for it.  Live slots must lie in
+ * [1, N); a slot >= N is treated as padding.
+ *
+ *   x          [B, 3*H*128]      BF16  q | k | v channels before the convolution
+ *   conv_w     [3, 4, H*128]     BF16  (part, tap, channel); tap 0 multiplies the oldest entry
+ *   conv_b     [3*H*128] or NULL BF16  convolution bias (NULL: none)
+ *   conv_state [N, 3*H*128, W]   BF16  per-slot window, W >= 3, in place
+ *   f_a        [B, 128]          BF16  low-rank gate input
+ *   beta       [B, H]            BF16  beta logits
+ *   a_log      [H]               FP32
+ *   dt_bias    [H*128]           FP32
+ *   slots      [B]               INT32
+ *   state      [N, H, 128, 128]  FP32  (slot, head, value row, key), in place
+ *   out        [B, H*128]        BF16
+ *   gate       [B, H*128]        BF16  output-gate logits
+ *   norm_w     [128]             BF16  RMSNorm weight
+ *   lower_bound, scale, eps            decay bound, q scale (1/sqrt(128)), RMSNorm eps
+ *   f_b        [H*128, 128]      BF16  gate projection
+ *   gate_mode  0 or 1: the accumulation structure of the gate projection
+ *              (0: one chain, 1: four chains over 32-column quarters).  This
+ *              library accumulates the projection exactly, so both modes
+ *              give the same bits (the correctly rounded FP32 sum).
+ *   ahead      prefetch distance in items (-1: library default, 0: off)
+ */
+kda_status kda_decode(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                      uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                      const float* a_log, const float* dt_bias, const int32_t* slots,
+                      float* state, uint16_t* out, const uint16_t* gate,
+                      const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                      const uint16_t* f_b, int B, int H, int N, int W, int gate_mode,
+                      int ahead, void* stream);
+
+/*
+ * kda_verify -- one speculative-verify step over T in [2, 8] tokens
+ * (KdaWide with tokens = T, optionally record = RecoverSSM).
+ *
+ * The same operands as kda_decode, with x, f_a, beta, gate and out holding
+ * B*T rows (row b*T + t is token t of request b) and slots of shape
+ * [B, slot_stride], slot_stride >= T.  Slot resolution (the page's verify
+ * branch): offset = accepted[b] - 1, the state is read from
+ * slots[b, offset], the convolution window of slots[b, 0] is read at columns
+ * offset .. offset+2 and rewritten at columns 0 .. T+1 (so W >= T + 2).
+ * A read slot <= 0 marks padding (B*T output rows of BF16 +0, nothing else
+ * touched).  Without record, the state after token t is written to
+ * slots[b, t] when that entry is in [1, N) and skipped otherwise.  With
+ * record, no state is written; instead
+ *   rec_u  [B, H, T, 128]  FP32  u of every value row and token
+ *   rec_kg [B, H, T, 256]  BF16  k (after SiLU, before the norm) | raw_g
+ * are written for live items (padded items leave them untouched), from which
+ * the state after any accepted prefix can be rebuilt from the checkpoint page
+ * that was read.
+ *   accepted [B] INT32, 1 <= accepted[b] <= T (a value outside that range
+ *            makes the item padding).
+ */
+kda_status kda_verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                      uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                      const float* a_log, const float* dt_bias, const int32_t* slots,
+                      float* state, uint16_t* out, const uint16_t* gate,
+                      const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                      const uint16_t* f_b, const int32_t* accepted, float* rec_u,
+                      uint16_t* rec_kg, int B, int H, int N, int W, int T, int slot_stride,
+                      int record, int gate_mode, int ahead, void* stream);
+
+/*
+ * kda_validate -- the host-side checks of kda_verify (T = 1 checks a decode
+ * call, with slot_stride and accepted ignored) without enqueuing anything.
+ * Touches no device memory and makes no HIP call: usable without a GPU.
+ */
+kda_status kda_validate(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                        uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                        const float* a_log, const float* dt_bias, const int32_t* slots,
+                        float* state, uint16_t* out, const uint16_t* gate,
+                        const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                        const uint16_t* f_b, const int32_t* accepted, float* rec_u,
+                        uint16_t* rec_kg, int B, int H, int N, int W, int T,
+                        int slot_stride, int record, int gate_mode);
+
+/* A static, human-readable name for a status code. */
+const char* kda_status_string(kda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

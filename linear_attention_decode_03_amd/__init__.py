@@ -1,0 +1,9 @@
+"""MI355X-native Kimi Delta Attention (KDA) decode / verify step.
+
+The computation lives in hand-written HIP kernels for gfx950 (csrc/kda.hip),
+exported through the C ABI declared in include/kda.h and built into
+libkda.so next to this file.  `kda` is the thin ctypes binding; `inputs`
+makes seeded synthetic operands.  Importing the package loads nothing.
+"""
+
+from .kda import kda_decode, kda_status_string, kda_validate, kda_verify, load_library  # noqa: F401

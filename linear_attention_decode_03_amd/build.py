@@ -1,0 +1,42 @@
+"""Builds the HIP library (libkda.so) in-tree for gfx950.
+
+The library is one translation unit, csrc/kda.hip, compiled with hipcc.
+Packed FP32 instructions are switched off (-packed-fp32-ops): the kernels
+are written for scalar FP32 FMAs.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "kda.hip")
+LIB = os.path.join(HERE, "libkda.so")
+INCLUDE = os.path.join(ROOT, "include")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+
+def hipcc_command(out: str = LIB) -> list:
+    return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-command-line-argument",
+            f"-I{INCLUDE}", "-o", out, SRC]
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compiles csrc/kda.hip into libkda.so next to this file (atomically)."""
+    tmp = LIB + ".tmp"
+    r = subprocess.run(hipcc_command(tmp), capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    if verbose and r.stderr:
+        print(r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle,
+element by element, on seeded inputs (contract in tests/_parity.py).
+
+Covers the five workloads at their full sizes (every item compared), ragged
+and degenerate shapes, padding and out-of-range tables, the invariants of
+the method on the GPU, and the launch on a non-default stream.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_decode_03_amd import inputs
+from linear_attention_decode_03_amd.inputs import copy_problem, to_bf16
+
+from . import _parity
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    from . import _gpu
+    from linear_attention_decode_03_amd import kda
+
+    kda.load_library()
+    return _gpu
+
+
+def gpu_step(gpu, p, ahead=-1, stream=None):
+    import torch
+
+    d = gpu.to_device(p)
+    gpu.run(d, ahead=ahead, stream=stream)
+    torch.cuda.synchronize()
+    return gpu.to_host(d)
+
+
+def check(gpu, p, label, ahead=-1):
+    say(f"[parity] {label}: B={p['B']} H={p['H']} T={p['T']} N={p['N']} W={p['W']} "
+        f"record={p['record']} gate_mode={p['gate_mode']}")
+    before = copy_problem(p)
+    ref = copy_problem(p)
+    taps = oracle.run(ref, taps=True)
+    got = gpu_step(gpu, p, ahead=ahead)
+    rep = _parity.compare_step(before, ref, got, taps)
+    say(f"[parity] {label}: ok {rep}")
+    return rep, got, ref
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size
+
+
+@pytest.mark.parametrize("name", list(inputs.CONFIGS))
+def test_config_parity(gpu, name):
+    p = inputs.make_problem(name)
+    rep, _, _ = check(gpu, p, name)
+    live = len(_parity._live_items(p))
+    assert rep["out_ties_used"] <= max(4, 0.002 * live * p["T"] * 128)
+
+
+# --------------------------------------------------------------------------
+# ragged shapes, padding, out-of-range tables, bias
+
+
+def test_ragged_decode_with_padding(gpu):
+    p = inputs.make_problem(dict(B=7, H=3, T=1, N=20, W=3, seed=101))
+    p["slots"][[1, 4]] = [0, -3]
+    p["slots"][5] = p["N"] + 2  # beyond the pool: treated as padding
+    check(gpu, p, "ragged decode")
+
+
+@pytest.mark.parametrize("T", [2, 3, 5, 6, 7, 8])
+def test_ragged_verify(gpu, T):
+    B, H = 5, 3
+    p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 3, seed=200 + T))
+    p["slots"][1, T - 1] = 0      # a skipped write target
+    p["accepted"][2] = T + 1      # out of range: padding
+    p["slots"][3, 0] = -1         # convolution slot out of range: padding
+    check(gpu, p, f"ragged verify T={T}")
+
+
+@pytest.mark.parametrize("T", [2, 8])
+def test_record_ragged(gpu, T):
+    B, H = 4, 5
+    p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=300 + T, record=1))
+    p["accepted"][2] = 0          # padding in record mode leaves the records untouched
+    check(gpu, p, f"record T={T}")
+
+
+def test_conv_bias(gpu):
+    for T in (1, 4):
+        cfg = dict(B=3, H=2, T=T, N=3 * T + 2, W=T + 2, seed=400 + T)
+        p = inputs.make_problem(cfg)
+        rng = np.random.default_rng(7)
+        p["conv_b"] = to_bf16(rng.standard_normal(3 * p["H"] * 128).astype(np.float32) * 0.3)
+        p["has_bias"] = 1
+        check(gpu, p, f"bias T={T}")
+
+
+def test_empty_batch(gpu):
+    import torch
+
+    p = inputs.make_problem(dict(B=0, H=2, T=1, N=3, W=3, seed=1))
+    before = copy_problem(p)
+    got = gpu_step(gpu, p)
+    assert np.array_equal(got["state"], before["state"])
+    assert np.array_equal(got["conv_state"], before["conv_state"])
+    torch.cuda.synchronize()
+
+
+def test_contract_errors_raise(gpu):
+    p = inputs.make_problem(dict(B=2, H=2, T=2, N=5, W=4, seed=3))
+    d = gpu.to_device(p)
+    with pytest.raises(ValueError):
+        d2 = dict(d)
+        d2["gate_mode"] = 2
+        gpu.run(d2)
+    with pytest.raises(ValueError):
+        d2 = dict(d)
+        d2["W"] = 3
+        d2["conv_state"] = d["conv_state"][:, :, :3].contiguous()
+        gpu.run(d2)   # W < T + 2
+
+
+# --------------------------------------------------------------------------
+# the method's invariants, on the GPU
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_identity_invariant_gpu(gpu, T):
+    """Decay 1 (lower_bound 0) and beta 0: every written page equals the
+    page read, bit for bit."""
+    cfg = dict(B=4, H=4, T=T, N=4 * T + 2, W=T + 2, seed=500 + T, lower_bound=0.0)
+    p = inputs.make_problem(cfg)
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, -200.0, np.float32))
+    say(f"[invariant] identity T={T}")
+    got = gpu_step(gpu, p)
+    for b in range(p["B"]):
+        src = p["slots"][b] if T == 1 else p["slots"][b, p["accepted"][b] - 1]
+        tgts = [p["slots"][b]] if T == 1 else list(p["slots"][b, :T])
+        for tgt in tgts:
+            assert np.array_equal(got["state"][tgt].view(np.uint32), p["state"][src].view(np.uint32))
+
+
+def test_delta_rule_beta_one_gpu(gpu):
+    """beta = 1: after the update S^T k_hat = v (k, v from the oracle, which
+    the GPU matches bit for bit)."""
+    p = inputs.make_problem(dict(B=4, H=4, T=1, N=10, W=3, seed=601))
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, 30.0, np.float32))
+    ref = copy_problem(p)
+    taps = oracle.run(ref, taps=True)
+    say("[invariant] delta rule beta=1")
+    got = gpu_step(gpu, p)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            S = got["state"][p["slots"][b], h].astype(np.float64)
+            k = taps["k"][b, h, 0].astype(np.float64)
+            kh = k / np.sqrt((k * k).sum() + 1e-6)
+            v = taps["v"][b, h, 0].astype(np.float64)
+            u = taps["u"][b, h, 0].astype(np.float64)
+            assert np.all(np.abs(S @ kh - v) <= 1e-5 * (np.abs(v) + np.abs(u) + 1e-3))
+
+
+@pytest.mark.parametrize("T", [2, 4, 8])
+def test_verify_equals_chained_decode_gpu(gpu, T):
+    """A T-token verify (accepted = 1) equals T chained decodes, on the GPU."""
+    import torch
+
+    B, H = 3, 4
+    p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=700 + T))
+    p["accepted"][:] = 1
+    say(f"[invariant] verify vs chained decode T={T}")
+    got_v = gpu_step(gpu, p)
+    chain = dict(p)
+    chain.update(T=1, W=3, slot_stride=1, record=0, accepted=None, rec_u=None, rec_kg=None)
+    chain["slots"] = np.ascontiguousarray(p["slots"][:, 0])
+    chain["conv_state"] = np.ascontiguousarray(p["conv_state"][:, :, :3])
+    d = gpu.to_device(chain)
+    for t in range(T):
+        rows = torch.as_tensor(np.arange(B) * T + t, device="cuda")
+        step = dict(d)
+        for key in ("x", "f_a", "beta", "gate"):
+            step[key] = d[key][rows].contiguous()
+        step["out"] = torch.zeros((B, H * 128), dtype=torch.bfloat16, device="cuda")
+        gpu.run(step)
+        torch.cuda.synchronize()
+        out_t = step["out"].view(torch.int16).cpu().numpy().view(np.uint16)
+        st = d["state"].cpu().numpy()
+        for b in range(B):
+            r = st[chain["slots"][b]].astype(np.float64)
+            g = got_v["state"][p["slots"][b, t]].astype(np.float64)
+            rms = np.sqrt((r * r).mean())
+            assert np.all(np.abs(g - r) <= 1e-5 * (np.abs(r) + rms))
+        o_r = inputs.from_bf16(out_t).astype(np.float64)
+        o_g = inputs.from_bf16(got_v["out"][np.arange(B) * T + t]).astype(np.float64)
+        assert np.all(np.abs(o_g - o_r) <= 2 * _parity.ulp_bf16(np.maximum(np.abs(o_r), 1e-3)))
+    conv = d["conv_state"].view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(B):
+        cs = chain["slots"][b]
+        assert np.array_equal(got_v["conv_state"][cs][:, T - 1:T + 2], conv[cs])
+
+
+def test_gate_modes_agree_gpu(gpu):
+    """gate_mode selects the accumulation structure; the projection is exact
+    here, so both modes give identical bits."""
+    p = inputs.make_problem(dict(B=6, H=4, T=3, N=19, W=5, seed=801))
+    say("[gate_mode] 0 vs 1")
+    a = gpu_step(gpu, copy_problem(p))
+    p["gate_mode"] = 1
+    b = gpu_step(gpu, p)
+    for k in ("state", "conv_state", "out"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_record_matches_plain_gpu(gpu):
+    """Record mode computes the same outputs and windows as a plain verify,
+    writes no state page, and its records replay to the plain states."""
+    T = 4
+    p = inputs.make_problem(dict(B=5, H=4, T=T, N=21, W=6, seed=901, record=1))
+    plain = copy_problem(p)
+    plain.update(record=0, rec_u=None, rec_kg=None)
+    say("[record] vs plain")
+    r = gpu_step(gpu, copy_problem(p))
+    q = gpu_step(gpu, plain)
+    assert np.array_equal(r["out"], q["out"])
+    assert np.array_equal(r["conv_state"], q["conv_state"])
+    assert np.array_equal(r["state"].view(np.uint32), p["state"].view(np.uint32))
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            S = p["state"][p["slots"][b, p["accepted"][b] - 1], h].astype(np.float64)
+            dt = p["dt_bias"][h * 128:(h + 1) * 128]
+            for t in range(T):
+                k = inputs.from_bf16(r["rec_kg"][b, h, t, :128]).astype(np.float64)
+                g = inputs.from_bf16(r["rec_kg"][b, h, t, 128:])
+                a = np.array([oracle.decay(float(p["a_log"][h]), float(g[f]), float(dt[f]),
+                                           p["lower_bound"]) for f in range(128)])
+                kh = k / np.sqrt((k * k).sum() + 1e-6)
+                S = S * a[None, :] + np.outer(r["rec_u"][b, h, t].astype(np.float64), kh)
+                ref = q["state"][p["slots"][b, t], h].astype(np.float64)
+                rms = np.sqrt((ref ** 2).mean())
+                assert np.all(np.abs(S - ref) <= 1e-4 * (np.abs(ref) + rms))
+
+
+def test_nondefault_stream(gpu):
+    import torch
+
+    p = inputs.make_problem(dict(B=4, H=8, T=1, N=9, W=3, seed=1001))
+    before = copy_problem(p)
+    ref = copy_problem(p)
+    taps = oracle.run(ref, taps=True)
+    s = torch.cuda.Stream()
+    d = gpu.to_device(p)
+    torch.cuda.synchronize()
+    say("[stream] non-default stream")
+    with torch.cuda.stream(s):
+        gpu.run(d, stream=s)
+    s.synchronize()
+    _parity.compare_step(before, ref, gpu.to_host(d), taps)
