@@ -118,11 +118,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), kCtrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, 0xf, 0xf, false);
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo)));
+}
+
+// The same 16-lane row sum for FP64 values (each half moved by DPP).
 __device__ __forceinline__ double row_sum16_f64(double v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp_f64<0xb1>(v);
+  v += dpp_f64<0x4e>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
   return v;
 }
 
@@ -134,6 +144,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPageBytes = kD * kD * 4;      // one (slot, head) page: 64 KiB
 constexpr int kRsrcWord3 = 0x00020000;       // gfx9 raw-buffer format word
+constexpr int kStream = 2;                   // cache policy: non-temporal (nt)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(float* state, int slot, int h, int H) {
   float* page = state + (static_cast<size_t>(slot) * H + h) * (kD * kD);
@@ -141,7 +152,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(float* state, int sl
 }
 
 __device__ __forceinline__ float4 load_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStream);
   return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                      __uint_as_float(v.w));
 }
@@ -150,7 +161,7 @@ __device__ __forceinline__ void store_f4(__amdgpu_buffer_rsrc_t r, int voff, int
   u32x4 v;
   v.x = __float_as_uint(f.x); v.y = __float_as_uint(f.y);
   v.z = __float_as_uint(f.z); v.w = __float_as_uint(f.w);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, kStream);
 }
 
 // ---- the step kernel -----------------------------------------------------
@@ -202,9 +213,12 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(const Args A) {
   __shared__ float sh_os[T][2];     // [token][wave 0, 1]
 
   // 1. State page into registers: one buffer resource per 64 KiB page, a
-  //    per-lane byte offset in one VGPR and the (i, j) offsets as scalars.
+  //    per-lane byte offset in one VGPR and the (i, j) offsets as immediates.
+  //    Thread (wave w, lane l) owns rows 32(l >> 4) + 8w + i, i < 8: every
+  //    16-byte access of a wave covers four 256-byte row segments 16 KiB
+  //    apart, which spreads each instruction over more HBM channels.
   const int c16 = lane & 15;
-  const int row0 = 32 * wave + (lane >> 4);
+  const int row0 = 32 * (lane >> 4) + 8 * wave;
   const int lane_off = (row0 * kD + 4 * c16) * 4;
   float4 st[8][2];
   {
@@ -212,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(const Args A) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) st[i][j] = load_f4(page, lane_off, 4 * i * kD * 4 + j * 256);
+      for (int j = 0; j < 2; ++j) st[i][j] = load_f4(page, lane_off, i * kD * 4 + j * 256);
   }
 
   // 2. Convolution + SiLU.  Threads 0-127 make q and k of channel tid,
@@ -282,24 +296,33 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(const Args A) {
   {
     const int fsub = tid >> 4;
     const int j0 = 8 * (tid & 15);
+    // Feature groups of G: all eight loads at once for decode; pairs for
+    // verify, where the state page occupies the registers longer.
+    constexpr int G = T == 1 ? 8 : 2;
 #pragma unroll 1
-    for (int i = 0; i < 8; ++i) {
-      const uint4 fb4 = *reinterpret_cast<const uint4*>(
-          A.f_b + (static_cast<size_t>(h) * kD + 16 * i + fsub) * kD + j0);
+    for (int i0 = 0; i0 < 8; i0 += G) {
+      uint4 fb[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        fb[g] = *reinterpret_cast<const uint4*>(
+            A.f_b + (static_cast<size_t>(h) * kD + 16 * (i0 + g) + fsub) * kD + j0);
 #pragma unroll 1
       for (int t = 0; t < T; ++t) {
         const uint4 fa4 = *reinterpret_cast<const uint4*>(A.f_a + (token0 + t) * kD + j0);
-        // A product of two BF16 values is exact in FP32; the sum is kept in FP64.
-        double acc = static_cast<double>(bf16_lo(fb4.x) * bf16_lo(fa4.x));
-        acc += static_cast<double>(bf16_hi(fb4.x) * bf16_hi(fa4.x));
-        acc += static_cast<double>(bf16_lo(fb4.y) * bf16_lo(fa4.y));
-        acc += static_cast<double>(bf16_hi(fb4.y) * bf16_hi(fa4.y));
-        acc += static_cast<double>(bf16_lo(fb4.z) * bf16_lo(fa4.z));
-        acc += static_cast<double>(bf16_hi(fb4.z) * bf16_hi(fa4.z));
-        acc += static_cast<double>(bf16_lo(fb4.w) * bf16_lo(fa4.w));
-        acc += static_cast<double>(bf16_hi(fb4.w) * bf16_hi(fa4.w));
-        acc = row_sum16_f64(acc);
-        if ((tid & 15) == 0) sh_g[t][16 * i + fsub] = static_cast<float>(acc);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          // A product of two BF16 values is exact in FP32; the sum is kept in FP64.
+          double acc = static_cast<double>(bf16_lo(fb[g].x) * bf16_lo(fa4.x));
+          acc += static_cast<double>(bf16_hi(fb[g].x) * bf16_hi(fa4.x));
+          acc += static_cast<double>(bf16_lo(fb[g].y) * bf16_lo(fa4.y));
+          acc += static_cast<double>(bf16_hi(fb[g].y) * bf16_hi(fa4.y));
+          acc += static_cast<double>(bf16_lo(fb[g].z) * bf16_lo(fa4.z));
+          acc += static_cast<double>(bf16_hi(fb[g].z) * bf16_hi(fa4.z));
+          acc += static_cast<double>(bf16_lo(fb[g].w) * bf16_lo(fa4.w));
+          acc += static_cast<double>(bf16_hi(fb[g].w) * bf16_hi(fa4.w));
+          acc = row_sum16_f64(acc);
+          if ((tid & 15) == 0) sh_g[t][16 * (i0 + g) + fsub] = static_cast<float>(acc);
+        }
       }
     }
   }
@@ -347,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(const Args A) {
         dot = fmaf(s[e], kh[e], dot);
       }
       dot = row_sum16(dot);
-      const int v = row0 + 4 * i;
+      const int v = row0 + i;
       const float u = (sh_v[t][v] - dot) * beta;
       float o = 0.0f;
 #pragma unroll
@@ -369,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(const Args A) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) store_f4(page, lane_off, 4 * i * kD * 4 + j * 256, st[i][j]);
+          for (int j = 0; j < 2; ++j) store_f4(page, lane_off, i * kD * 4 + j * 256, st[i][j]);
       }
     }
   }
