@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-PROFILE_PMC = os.path.join(ROOT, "profiles", "kda_decode_b256_pmc.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_03_amd", "csrc", "kda.hip")
 D = 128
 
@@ -57,13 +57,14 @@ def algorithmic_bytes(p) -> int:
     return int(total)
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source (else None)."""
-    if not os.path.exists(PROFILE_PMC):
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"kda_{workload}_pmc.txt")
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(PROFILE_PMC):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
@@ -168,7 +169,7 @@ def main():
     items = p["B"] * p["H"]
     abytes = algorithmic_bytes(p)
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(args.workload)
     result = {
         "metric": "KDA decode (request,head)-steps/sec and achieved HBM GB/s (% of peak)",
         "value": items / (ms_per_step * 1e-3),
