@@ -70,6 +70,31 @@ def test_config_parity(gpu, name):
     assert rep["out_ties_used"] <= max(4, 0.002 * live * p["T"] * 128)
 
 
+@pytest.mark.parametrize("name,steps", [("decode_b256", 4), ("verify_t4", 3)])
+def test_chained_launches(gpu, name, steps):
+    """Several launches back to back on the same pools (the state evolves),
+    compared with the oracle after every launch.  A store whose data is
+    corrupted in flight shows up here even when it strikes a few pages per
+    launch."""
+    import torch
+
+    p = inputs.make_problem(name)
+    ref = copy_problem(p)
+    d = gpu.to_device(p)
+    for k in range(steps):
+        before = copy_problem(ref)
+        taps = oracle.run(ref, taps=True)
+        gpu.run(d)
+        torch.cuda.synchronize()
+        got = gpu.to_host(d)
+        say(f"[chain] {name} launch {k}")
+        _parity.compare_step(before, ref, got, taps)
+        # the next launch starts from the GPU's own pools, as a caller's would
+        ref["state"] = got["state"].copy()
+        ref["conv_state"] = got["conv_state"].copy()
+        ref["out"] = got["out"].copy()
+
+
 # --------------------------------------------------------------------------
 # ragged shapes, padding, out-of-range tables, bias
 
@@ -225,16 +250,16 @@ def test_gate_modes_agree_gpu(gpu):
 
 
 def test_record_matches_plain_gpu(gpu):
-    """Record mode computes the same outputs and windows as a plain verify,
-    writes no state page, and its records replay to the plain states."""
+    """Record mode (closed-form kernel) and a plain verify of the same inputs
+    both match the oracle; record mode writes no state page, leaves the same
+    convolution windows, and its records replay to the plain states."""
     T = 4
     p = inputs.make_problem(dict(B=5, H=4, T=T, N=21, W=6, seed=901, record=1))
     plain = copy_problem(p)
     plain.update(record=0, rec_u=None, rec_kg=None)
     say("[record] vs plain")
-    r = gpu_step(gpu, copy_problem(p))
-    q = gpu_step(gpu, plain)
-    assert np.array_equal(r["out"], q["out"])
+    rep_r, r, _ = check(gpu, copy_problem(p), "record T=4")
+    rep_q, q, _ = check(gpu, plain, "plain T=4")
     assert np.array_equal(r["conv_state"], q["conv_state"])
     assert np.array_equal(r["state"].view(np.uint32), p["state"].view(np.uint32))
     for b in range(p["B"]):
@@ -251,6 +276,46 @@ def test_record_matches_plain_gpu(gpu):
                 ref = q["state"][p["slots"][b, t], h].astype(np.float64)
                 rms = np.sqrt((ref ** 2).mean())
                 assert np.all(np.abs(S - ref) <= 1e-4 * (np.abs(ref) + rms))
+
+
+@pytest.mark.parametrize("lb", [-12.0, 10.0, -10.0])
+def test_record_decay_bound_paths(gpu, lb):
+    """|lower_bound| > 10 takes the token-by-token record kernel, <= 10 the
+    closed-form one; both match the oracle (10 is the edge of the closed form)."""
+    T = 8
+    p = inputs.make_problem(dict(B=6, H=3, T=T, N=49, W=10, seed=950, record=1,
+                                 lower_bound=lb))
+    check(gpu, p, f"record lower_bound={lb}")
+
+
+def test_silu_every_bf16_input_gpu(gpu):
+    """The kernel's SiLU (fast FP32 path with a rounding-boundary test, FP64
+    otherwise) against the oracle's, for every finite BF16 convolution sum:
+    tap weights [0, 0, 0, 1] make the k-channel sum equal x exactly, and
+    record mode stores k."""
+    B, H, T = 64, 4, 8
+    p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=960, record=1))
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    vals = bits[finite]
+    dim = H * 128
+    n = B * T * dim
+    xk = np.resize(vals, n).reshape(B * T, dim)
+    p["x"][:, dim:2 * dim] = xk
+    p["conv_w"][1] = to_bf16(np.array([0, 0, 0, 1], np.float32))[:, None]
+    say(f"[silu] {vals.size} BF16 inputs")
+    got = gpu_step(gpu, p)
+    k_gpu = got["rec_kg"][..., :128]                                    # [B, H, T, 128]
+    xs = inputs.from_bf16(xk).reshape(B, T, H, 128).transpose(0, 2, 1, 3)
+    # The convolution's FP32 sum fma(x, 1, +0) is x, except that -0 becomes +0.
+    sums = inputs.from_bf16(vals) + np.float32(0.0)
+    want = np.array([oracle.silu_bf16(float(x)) for x in sums], dtype=np.float32)
+    lut = dict(zip(vals.tolist(), to_bf16(want).tolist()))
+    xb = xk.reshape(B, T, H, 128).transpose(0, 2, 1, 3)
+    ref = np.vectorize(lut.__getitem__, otypes=[np.uint16])(xb)
+    bad = np.nonzero(k_gpu != ref)
+    assert bad[0].size == 0, (f"{bad[0].size} SiLU mismatches, first x="
+                              f"{xs[tuple(d[0] for d in bad)]}")
 
 
 def test_nondefault_stream(gpu):

@@ -270,10 +270,10 @@ def test_decay_through_state(oracle_lib):
 def test_silu_textbook(oracle_lib):
     xs = np.concatenate([np.linspace(-12, 12, 2001), [-100.0, -88.0, 0.0, 1e-3, 50.0]])
     xs = from_bf16(to_bf16(xs.astype(np.float32)))  # BF16-exact inputs, as the conv sees
-    for x in xs:
+    want = bf16_of_f64(silu64(xs.astype(np.float64)))
+    for x, w in zip(xs, want):
         got = oracle_lib.silu_bf16(float(x))
-        want = float(bf16_of_f64(silu64(float(x)))[()])
-        assert got == want or (math.isnan(got) and math.isnan(want)), x
+        assert got == float(w) or (math.isnan(got) and math.isnan(w)), x
 
 
 @pytest.mark.parametrize("T", [1, 3])
@@ -361,7 +361,7 @@ def test_zero_state_closed_form(oracle_lib):
         for h in range(p["H"]):
             k = taps["k"][b, h, 0].astype(np.float64)
             v = taps["v"][b, h, 0].astype(np.float64)
-            beta = 1.0 / (1.0 + np.exp(-float(from_bf16(p["beta"][b, h])[()])))
+            beta = 1.0 / (1.0 + np.exp(-float(from_bf16(p["beta"][b:b + 1, h])[0])))
             kh = k / np.sqrt((k * k).sum() + 1e-6)
             S = p["state"][int(p["slots"][b]), h].astype(np.float64)
             assert np.allclose(S, np.outer(v * beta, kh), rtol=1e-6, atol=1e-9)
