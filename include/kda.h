@@ -90,7 +90,10 @@ typedef enum kda_status {
  *              (0: one chain, 1: four chains over 32-column quarters).  This
  *              library accumulates the projection exactly, so both modes
  *              give the same bits (the correctly rounded FP32 sum).
- *   ahead      prefetch distance in items (-1: library default, 0: off)
+ *   ahead      prefetch distance in items: each workgroup touches the state
+ *              page of the item that many positions later (rounded up to a
+ *              multiple of 8).  A hint only; results are identical for every
+ *              value.  -1 takes the library default (off).
  */
 kda_status kda_decode(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
                       uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,

@@ -56,6 +56,7 @@ struct Args {
   uint16_t* rec_kg;
   float lower_bound, scale, eps;
   int B, H, N, W, slot_stride;
+  int ahead;  // prefetch distance in items (0: off), a multiple of 8
 };
 
 // ---- BF16 storage --------------------------------------------------------
@@ -269,6 +270,42 @@ __device__ __forceinline__ bool resolve(const Args& A, Item& it) {
     it.cs = A.slots[static_cast<size_t>(it.b) * A.slot_stride];
     return it.rs > 0 && it.rs < A.N && it.cs >= 0 && it.cs < A.N;
   }
+}
+
+// Prefetch (the page's prefetch_next): touch every 128-byte line of the
+// state page that item blockIdx + ahead will read, so that it is on its way
+// into the L2 of the XCD that runs that item (workgroups go round-robin to
+// the 8 XCDs; ahead is a multiple of 8) and into the memory-side cache.  Two
+// 4-byte loads per thread with the default cache policy (so the lines are
+// kept), issued after the item's own page loads so that the in-order
+// retirement of loads does not hold up the input phase; the values are only
+// kept alive by a test that is never true at run time.  Measured on MI355X
+// this never pays: at 8 MiB of pages in flight per XCD against a 4 MB L2 the
+// touched lines are mostly gone before use, so it adds reads (decode B=256:
+// +5 % at ahead 256, +28 % at 1024); the default is off.
+template <int T>
+__device__ __forceinline__ void prefetch_page(const Args& A, float& sink) {
+  sink = 0.0f;
+  const int item = static_cast<int>(blockIdx.x) + A.ahead;
+  if (A.ahead <= 0 || item >= static_cast<int>(gridDim.x)) return;
+  const int b = item / A.H, h = item % A.H;
+  int slot;
+  if constexpr (T == 1) {
+    slot = A.slots[b];
+  } else {
+    const int acc = A.accepted[b];
+    const int lim = T < A.slot_stride ? T : A.slot_stride;
+    if (acc < 1 || acc > lim) return;
+    slot = A.slots[static_cast<size_t>(b) * A.slot_stride + acc - 1];
+  }
+  if (slot <= 0 || slot >= A.N) return;
+  const float* page = A.state + (static_cast<size_t>(slot) * A.H + h) * (kD * kD);
+  const int line = 64 * static_cast<int>(threadIdx.x);  // floats: 256 B per thread
+  sink = page[line] + page[line + 32];
+}
+
+__device__ __forceinline__ void keep_alive(const Args& A, float sink) {
+  if (A.B < 0 && sink == 0.0f) A.out[0] = 0;  // B < 0 never reaches a kernel
 }
 
 template <int T>
@@ -573,6 +610,8 @@ void kda_step_kernel(const Args A) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) st[i][j] = load_f4(page, lane_off, i * kD * 4 + j * 256);
   }
+  float sink;
+  prefetch_page<T>(A, sink);
 
   // 2. Inputs.
   conv_compute<T, kRecord>(A, it, sh, co);
@@ -641,6 +680,7 @@ void kda_step_kernel(const Args A) {
 
   // 4. Gated RMSNorm.
   gated_rmsnorm<T>(A, it, sh, sh.o, oo);
+  keep_alive(A, sink);
 }
 
 // ---- record mode (RecoverSSM verify): all tokens from one pass over S0 -------
@@ -682,6 +722,8 @@ void kda_record_kernel(const Args A) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) st[tile][q] = load_f4(page, voff, tile * 16 * kD * 4 + 64 * q);
   }
+  float sink;
+  prefetch_page<T>(A, sink);
 
   // 2. Inputs.
   conv_silu<T, true, kBias>(A, it, sh);
@@ -772,6 +814,7 @@ void kda_record_kernel(const Args A) {
 
   // 6. Gated RMSNorm.
   gated_rmsnorm<T>(A, it, sh, sh.u.out.o, oo);
+  keep_alive(A, sink);
 }
 
 // ---- host side -------------------------------------------------------------
@@ -836,12 +879,23 @@ kda_status launch(const Args& A, int T, hipStream_t stream) {
   }
 }
 
+// The prefetch distance: -1 takes the library default (off: the step is at
+// its measured HBM ceiling without it), other values are rounded up to a
+// multiple of 8 so that the prefetching workgroup and the one that reads the
+// page sit on the same XCD.
+constexpr int kDefaultAhead = 0;
+
+int resolve_ahead(int ahead) {
+  if (ahead < 0) ahead = kDefaultAhead;
+  return (ahead + 7) & ~7;
+}
+
 Args pack(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
           uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta, const float* a_log,
           const float* dt_bias, const int32_t* slots, float* state, uint16_t* out,
           const uint16_t* gate, const uint16_t* norm_w, float lower_bound, float scale,
           float eps, const uint16_t* f_b, const int32_t* accepted, float* rec_u,
-          uint16_t* rec_kg, int B, int H, int N, int W, int slot_stride) {
+          uint16_t* rec_kg, int B, int H, int N, int W, int slot_stride, int ahead) {
   Args A;
   A.x = x; A.conv_w = conv_w; A.conv_b = conv_b; A.conv_state = conv_state; A.f_a = f_a;
   A.beta = beta; A.a_log = a_log; A.dt_bias = dt_bias; A.slots = slots; A.state = state;
@@ -849,6 +903,7 @@ Args pack(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
   A.rec_u = rec_u; A.rec_kg = rec_kg;
   A.lower_bound = lower_bound; A.scale = scale; A.eps = eps;
   A.B = B; A.H = H; A.N = N; A.W = W; A.slot_stride = slot_stride;
+  A.ahead = resolve_ahead(ahead);
   return A;
 }
 
@@ -866,7 +921,7 @@ kda_status kda_validate(const uint16_t* x, const uint16_t* conv_w, const uint16_
                         int record, int gate_mode) {
   const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
                       out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg,
-                      B, H, N, W, T == 1 ? 1 : slot_stride);
+                      B, H, N, W, T == 1 ? 1 : slot_stride, 0);
   return check(A, T, record, gate_mode);
 }
 
@@ -877,10 +932,9 @@ kda_status kda_decode(const uint16_t* x, const uint16_t* conv_w, const uint16_t*
                       const uint16_t* norm_w, float lower_bound, float scale, float eps,
                       const uint16_t* f_b, int B, int H, int N, int W, int gate_mode, int ahead,
                       void* stream) {
-  (void)ahead;
   const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
                       out, gate, norm_w, lower_bound, scale, eps, f_b, nullptr, nullptr,
-                      nullptr, B, H, N, W, 1);
+                      nullptr, B, H, N, W, 1, ahead);
   const kda_status s = check(A, 1, 0, gate_mode);
   if (s != KDA_OK || B == 0) return s;
   return launch<false>(A, 1, static_cast<hipStream_t>(stream));
@@ -894,11 +948,10 @@ kda_status kda_verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t*
                       const uint16_t* f_b, const int32_t* accepted, float* rec_u,
                       uint16_t* rec_kg, int B, int H, int N, int W, int T, int slot_stride,
                       int record, int gate_mode, int ahead, void* stream) {
-  (void)ahead;
   if (T == 1) return KDA_ERR_TOKENS;  // a one-token step is kda_decode
   const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
                       out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg,
-                      B, H, N, W, slot_stride);
+                      B, H, N, W, slot_stride, ahead);
   const kda_status s = check(A, T, record, gate_mode);
   if (s != KDA_OK || B == 0) return s;
   return record ? launch<true>(A, T, static_cast<hipStream_t>(stream))

@@ -159,3 +159,38 @@ def live_items(p: dict) -> np.ndarray:
         rs = p["slots"][np.arange(B), p["accepted"] - 1]
     live_b = np.nonzero(rs > 0)[0]
     return (live_b[:, None] * H + np.arange(H)[None, :]).reshape(-1).astype(np.int32)
+
+
+# The replay workload: a record-mode verify's records applied to checkpoint
+# pages.  B=128 requests, H=32 heads, T=8 recorded tokens, accepted counts
+# n ~ U{0..8}; checkpoint and target slots are distinct pool entries.
+REPLAY_CONFIGS = {
+    "replay_t8": dict(B=128, H=32, T=8, N=257, seed=5),
+}
+
+
+def make_replay_problem(name_or_cfg="replay_t8", seed=None, **override) -> dict:
+    """Seeded replay operands: state pool ~N(0, 0.02), records with k ~N(0, 1)
+    and raw_g ~N(0, 0.57) in BF16 (the spread of a BF16 projection of the
+    verify workload), u ~N(0, 0.5) in FP32, A_log ~U(-1, 1),
+    dt_bias ~N(0, 0.1), lower_bound = -5; src and dst slots are 2B distinct
+    entries of 1..N-1."""
+    cfg = dict(REPLAY_CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    cfg.update(override)
+    if seed is not None:
+        cfg["seed"] = seed
+    B, H, T, N = (int(cfg[k]) for k in ("B", "H", "T", "N"))
+    rng = np.random.default_rng(int(cfg.get("seed", 0)))
+    r = dict(B=B, H=H, T=T, N=N, lower_bound=float(cfg.get("lower_bound", -5.0)))
+    r["state"] = _normal(rng, (N, H, HEAD_DIM, HEAD_DIM), 0.02)
+    k = to_bf16(_normal(rng, (B, H, T, HEAD_DIM), 1.0))
+    g = to_bf16(_normal(rng, (B, H, T, HEAD_DIM), 0.57))
+    r["rec_kg"] = np.ascontiguousarray(np.concatenate([k, g], axis=3))
+    r["rec_u"] = _normal(rng, (B, H, T, HEAD_DIM), 0.5)
+    r["a_log"] = rng.uniform(-1.0, 1.0, size=H).astype(np.float32)
+    r["dt_bias"] = _normal(rng, (H * HEAD_DIM,), 0.1)
+    slots = rng.permutation(np.arange(1, N, dtype=np.int32))[: 2 * B]
+    r["src"] = np.ascontiguousarray(slots[:B])
+    r["dst"] = np.ascontiguousarray(slots[B:])
+    r["n"] = rng.integers(0, T + 1, size=B).astype(np.int32)
+    return r

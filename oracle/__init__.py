@@ -67,6 +67,8 @@ def _load():
         lib.kda_oracle_run.restype = ctypes.c_int
         lib.kda_oracle_run.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(_Taps)]
+        lib.kda_oracle_replay.restype = ctypes.c_int
+        lib.kda_oracle_replay.argtypes = [ctypes.c_void_p]
         lib.kda_oracle_silu_bf16.restype = ctypes.c_float
         lib.kda_oracle_silu_bf16.argtypes = [ctypes.c_float]
         lib.kda_oracle_decay.restype = ctypes.c_float
@@ -129,6 +131,36 @@ def run(p: dict, items=None, taps: bool = False):
     if status:
         raise ValueError(f"oracle rejected the problem (status {status})")
     return tap_arrays
+
+
+class _ReplayProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "H", "N", "T")] + \
+               [("lower_bound", ctypes.c_float)] + \
+               [(n, ctypes.c_void_p) for n in
+                ("rec_u", "rec_kg", "a_log", "dt_bias", "src", "dst", "n", "state")]
+
+
+_REPLAY_LAYOUT = {"rec_u": np.float32, "rec_kg": np.uint16, "a_log": np.float32,
+                  "dt_bias": np.float32, "src": np.int32, "dst": np.int32, "n": np.int32,
+                  "state": np.float32}
+
+
+def replay(r: dict):
+    """RecoverSSM replay on host arrays (see kda_oracle_replay in the C file):
+    r holds B, H, N, T, lower_bound and the arrays of _REPLAY_LAYOUT; `state`
+    is updated in place."""
+    lib = _load()
+    ptrs = {}
+    for k, dt in _REPLAY_LAYOUT.items():
+        a = r[k]
+        if a.dtype != dt or not a.flags["C_CONTIGUOUS"]:
+            raise TypeError(f"replay operand {k}: need contiguous {dt.__name__}")
+        ptrs[k] = a.ctypes.data
+    prob = _ReplayProblem(B=int(r["B"]), H=int(r["H"]), N=int(r["N"]), T=int(r["T"]),
+                          lower_bound=float(r["lower_bound"]), **ptrs)
+    status = lib.kda_oracle_replay(ctypes.byref(prob))
+    if status:
+        raise ValueError(f"oracle rejected the replay (status {status})")
 
 
 def silu_bf16(x: float) -> float:

@@ -353,3 +353,56 @@ int kda_oracle_run(const kda_oracle_problem* P, int gate_mode, const int32_t* it
   }
   return 0;
 }
+
+/* ---- RecoverSSM replay ------------------------------------------------- */
+
+/* After a record-mode verify, the state after the first n accepted tokens is
+ * rebuilt from the checkpoint page that verify read and its records, token by
+ * token, with the step's own arithmetic:
+ *   k_hat = k * (sum k^2 + 1e-6)^-1/2   (k: the recorded BF16 key, pre-norm)
+ *   a     = decay(A_log[h], raw_g, dt_bias[h*128 + f], lower_bound)
+ *   s     = fmaf(k_hat[key], u[v], s * a[key])   for every (v, key).
+ * n = 0 copies the checkpoint.  Items whose slots fall outside [1, N) or whose
+ * n falls outside [0, T] are skipped. */
+typedef struct kda_oracle_replay_problem {
+  int B, H, N, T;
+  float lower_bound;
+  const float* rec_u;      /* [B, H, T, 128] */
+  const uint16_t* rec_kg;  /* [B, H, T, 256]: k | raw_g */
+  const float* a_log;      /* [H] */
+  const float* dt_bias;    /* [H*128] */
+  const int32_t* src;      /* [B] checkpoint slot */
+  const int32_t* dst;      /* [B] slot to write */
+  const int32_t* n;        /* [B] tokens to apply */
+  float* state;            /* [N, H, 128, 128] */
+} kda_oracle_replay_problem;
+
+int kda_oracle_replay(const kda_oracle_replay_problem* P) {
+  if (P->T < 1 || P->T > MAX_T || P->B < 0 || P->H < 1 || P->N < 1) return 5;
+  for (int b = 0; b < P->B; ++b) {
+    const int src = P->src[b], dst = P->dst[b], n = P->n[b];
+    if (src <= 0 || src >= P->N || dst <= 0 || dst >= P->N || n < 0 || n > P->T) continue;
+    for (int h = 0; h < P->H; ++h) {
+      float S[D][D];
+      memcpy(S, P->state + (((size_t)src * P->H + h) * D) * D, sizeof(S));
+      for (int t = 0; t < n; ++t) {
+        const size_t rec = ((size_t)b * P->H + h) * P->T + t;
+        const uint16_t* kg = P->rec_kg + rec * 2 * D;
+        const float* u = P->rec_u + rec * D;
+        double sk = 0.0;
+        for (int c = 0; c < D; ++c) sk += (double)bf16_to_float(kg[c]) * (double)bf16_to_float(kg[c]);
+        const float fk = rsqrt_f32((float)sk + 1.0e-6f);
+        float k_hat[D], a[D];
+        for (int c = 0; c < D; ++c) {
+          k_hat[c] = bf16_to_float(kg[c]) * fk;
+          a[c] = kda_oracle_decay(P->a_log[h], bf16_to_float(kg[D + c]),
+                                  P->dt_bias[(size_t)h * D + c], P->lower_bound);
+        }
+        for (int v = 0; v < D; ++v)
+          for (int k = 0; k < D; ++k) S[v][k] = fmaf(k_hat[k], u[v], S[v][k] * a[k]);
+      }
+      memcpy(P->state + (((size_t)dst * P->H + h) * D) * D, S, sizeof(S));
+    }
+  }
+  return 0;
+}

@@ -134,6 +134,19 @@ def test_conv_bias(gpu):
         check(gpu, p, f"bias T={T}")
 
 
+@pytest.mark.parametrize("name", ["decode_b64", "verify_t4", "verify_record_t8"])
+def test_prefetch_changes_nothing(gpu, name):
+    """The prefetch distance is a hint: every value gives identical bits."""
+    p = inputs.make_problem(name)
+    say(f"[prefetch] {name}")
+    base = gpu_step(gpu, copy_problem(p), ahead=0)
+    for ahead in (8, 100, 1024):
+        got = gpu_step(gpu, copy_problem(p), ahead=ahead)
+        for k in ("state", "conv_state", "out", "rec_u", "rec_kg"):
+            if base[k] is not None:
+                assert np.array_equal(base[k].view(np.uint8), got[k].view(np.uint8)), (ahead, k)
+
+
 def test_empty_batch(gpu):
     import torch
 

@@ -28,7 +28,9 @@ MUTANTS = [
     ("k not normalised", "k_hat[t][c] = Y[1][t][c] * fk;", "k_hat[t][c] = Y[1][t][c];"),
     ("scale on k instead of q", "q_hat[t][c] = (Y[0][t][c] * fq) * P->scale;\n      k_hat[t][c] = Y[1][t][c] * fk;",
      "q_hat[t][c] = Y[0][t][c] * fq;\n      k_hat[t][c] = (Y[1][t][c] * fk) * P->scale;"),
-    ("k norm epsilon dropped", "rsqrt_f32((float)sk + 1.0e-6f)", "rsqrt_f32((float)sk)"),
+    ("k norm epsilon dropped",
+     "float fq = rsqrt_f32((float)sq + 1.0e-6f);\n    float fk = rsqrt_f32((float)sk + 1.0e-6f);",
+     "float fq = rsqrt_f32((float)sq + 1.0e-6f);\n    float fk = rsqrt_f32((float)sk);"),
     ("q norm epsilon dropped", "rsqrt_f32((float)sq + 1.0e-6f)", "rsqrt_f32((float)sq)"),
     ("gate projection transposed", "g += (double)bf16_to_float(row[j])",
      "g += (double)bf16_to_float(P->f_b[((size_t)h * D + j) * D + f])"),
@@ -62,6 +64,15 @@ MUTANTS = [
      "if (*read_slot < 0 || *read_slot >= P->N) return 0;"),
     ("record mode still writes state", "    } else {\n      /* State write-back",
      "    }\n    {\n      /* State write-back"),
+    ("replay u by key instead of value row", "fmaf(k_hat[k], u[v], S[v][k] * a[k])",
+     "fmaf(k_hat[k], u[k], S[v][k] * a[k])"),
+    ("replay norm epsilon dropped", "const float fk = rsqrt_f32((float)sk + 1.0e-6f);",
+     "const float fk = rsqrt_f32((float)sk);"),
+    ("replay without decay", "fmaf(k_hat[k], u[v], S[v][k] * a[k])", "fmaf(k_hat[k], u[v], S[v][k])"),
+    ("replay with the raw key", "k_hat[c] = bf16_to_float(kg[c]) * fk;", "k_hat[c] = bf16_to_float(kg[c]);"),
+    ("replay reads the wrong record token", "const size_t rec = ((size_t)b * P->H + h) * P->T + t;",
+     "const size_t rec = ((size_t)b * P->H + h) * P->T;"),
+    ("replay applies one token too many", "for (int t = 0; t < n; ++t) {", "for (int t = 0; t <= n && t < P->T; ++t) {"),
 ]
 
 

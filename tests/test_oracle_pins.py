@@ -16,6 +16,7 @@ formulation.  Which step each pin covers:
   recurrence order and orientation .... test_delta_rule_*, test_zero_state_closed_form
   verify slots / per-token writes ..... test_verify_equals_chained_decode
   record outputs ...................... test_record_replay
+  RecoverSSM replay ................... test_replay_*
   gated RMSNorm ....................... test_rmsnorm_closed_form, test_zero_state_closed_form
   everything together ................. test_matrix_form_cross_check
 """
@@ -489,3 +490,70 @@ def test_matrix_form_cross_check(oracle_lib, name, T):
                 rms = math.sqrt((ref ** 2).mean())
                 assert np.all(np.abs(g - ref) <= 1e-5 * (np.abs(ref) + rms))
     assert ties[0] <= 0.05 * p["B"] * p["H"] * T * 5 * D
+
+
+# --------------------------------------------------------------------------
+# RecoverSSM replay: checkpoint + records -> the state after n tokens
+
+
+def replay_from_record(p, n):
+    """A replay problem that applies the records of record-mode problem p
+    (after its run) to the pages p read, writing to fresh slots."""
+    B, H, T, N = p["B"], p["H"], p["T"], p["N"]
+    src = np.array([int(p["slots"][b, p["accepted"][b] - 1]) for b in range(B)], np.int32)
+    state = np.concatenate([p["state"], np.zeros((B,) + p["state"].shape[1:], np.float32)])
+    return dict(B=B, H=H, T=T, N=N + B, lower_bound=p["lower_bound"], rec_u=p["rec_u"],
+                rec_kg=p["rec_kg"], a_log=p["a_log"], dt_bias=p["dt_bias"], src=src,
+                dst=np.arange(N, N + B, dtype=np.int32), n=np.asarray(n, np.int32), state=state)
+
+
+def test_replay_matches_plain_verify(oracle_lib):
+    """Replaying the first n records from the checkpoint gives, bit for bit,
+    the state a plain verify of the same inputs writes after token n; n = 0
+    copies the checkpoint."""
+    T = 6
+    p = small(T=T, B=5, H=2, seed=61, record=1)
+    plain = inputs.copy_problem(p)
+    plain.update(record=0, rec_u=None, rec_kg=None)
+    oracle_lib.run(p)
+    oracle_lib.run(plain)
+    n = [0, 1, 3, 6, 4]
+    r = replay_from_record(p, n)
+    before = r["state"].copy()
+    oracle_lib.replay(r)
+    for b in range(p["B"]):
+        got = r["state"][r["dst"][b]]
+        want = before[r["src"][b]] if n[b] == 0 else plain["state"][int(plain["slots"][b, n[b] - 1])]
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), b
+    assert np.array_equal(r["state"][:p["N"]], before[:p["N"]])  # checkpoints untouched
+
+
+def test_replay_skips_invalid(oracle_lib):
+    r = inputs.make_replay_problem(dict(B=4, H=2, T=3, N=12, seed=7))
+    r["src"][0] = 0
+    r["dst"][1] = r["N"]
+    r["n"][2] = 4
+    before = r["state"].copy()
+    oracle_lib.replay(r)
+    for b in (0, 1, 2):
+        assert np.array_equal(r["state"][r["dst"][b] % r["N"]], before[r["dst"][b] % r["N"]])
+    assert not np.array_equal(r["state"][r["dst"][3]], before[r["dst"][3]]) or r["n"][3] == 0
+
+
+def test_replay_closed_form(oracle_lib):
+    """No decay (lower_bound 0): S_n = S_0 + sum_t k_hat_t u_t^T, an
+    independent float64 sum of outer products."""
+    r = inputs.make_replay_problem(dict(B=3, H=2, T=5, N=10, seed=9, lower_bound=0.0))
+    r["n"][:] = [5, 2, 3]
+    before = r["state"].copy()
+    oracle_lib.replay(r)
+    for b in range(r["B"]):
+        for h in range(r["H"]):
+            S = before[r["src"][b], h].astype(np.float64)
+            for t in range(int(r["n"][b])):
+                k = from_bf16(r["rec_kg"][b, h, t, :D]).astype(np.float64)
+                kh = k / np.sqrt((k * k).sum() + 1e-6)
+                S = S + np.outer(r["rec_u"][b, h, t].astype(np.float64), kh)
+            got = r["state"][r["dst"][b], h].astype(np.float64)
+            rms = math.sqrt((S ** 2).mean())
+            assert np.all(np.abs(got - S) <= 1e-5 * (np.abs(S) + rms))
