@@ -13,6 +13,10 @@ duration, measured with HIP events around each launch on the launch stream;
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --mode copy      # 1 GiB device copies (counter calibration)
+
+Workloads: tiny_decode, decode_b64, decode_b256 (default), verify_t4,
+verify_record_t8 (the step), and replay_t8 (the RecoverSSM replay of
+recorded tokens onto checkpoint pages).
 """
 
 import argparse
@@ -57,6 +61,20 @@ def algorithmic_bytes(p) -> int:
     return int(total)
 
 
+def replay_algorithmic_bytes(r) -> int:
+    """Bytes one replay launch must move: per valid (request, head) the 64 KiB
+    checkpoint page read and the 64 KiB page written, and per applied token
+    its records (512 B of u, 512 B of k | raw_g); the three slot tables;
+    A_log and dt_bias once."""
+    B, H, T, N = r["B"], r["H"], r["T"], r["N"]
+    total = 0
+    for b in range(B):
+        src, dst, n = int(r["src"][b]), int(r["dst"][b]), int(r["n"][b])
+        if 0 < src < N and 0 < dst < N and 0 <= n <= T:
+            total += H * (2 * 65536 + n * 1024)
+    return int(total + 3 * B * 4 + H * 4 + H * D * 4)
+
+
 def measured_traffic(workload):
     """HBM bytes per launch from the committed counter summary of this
     workload, if it was taken on the current kernel source (else None)."""
@@ -77,9 +95,10 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(p, min_seconds=10.0):
+def cpu_baseline(p, replay=False, min_seconds=10.0):
     """The oracle as it is (single-threaded C) on the same workload: whole
-    passes over all items until at least `min_seconds` have elapsed."""
+    passes over all items (the step, or the replay) until at least
+    `min_seconds` have elapsed."""
     import oracle
     from linear_attention_decode_03_amd.inputs import copy_problem
 
@@ -88,7 +107,10 @@ def cpu_baseline(p, min_seconds=10.0):
     n_items = p["B"] * p["H"]
     done, t0 = 0, time.perf_counter()
     while True:
-        oracle.run(q)
+        if replay:
+            oracle.replay(q)
+        else:
+            oracle.run(q)
         done += n_items
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -141,12 +163,23 @@ def main():
     from tests import _gpu
 
     kda.load_library()
-    p = inputs.make_problem(args.workload)
+    replay = args.workload in inputs.REPLAY_CONFIGS
+    if replay:
+        p = inputs.make_replay_problem(args.workload)
+    else:
+        p = inputs.make_problem(args.workload)
     print(f"[bench] workload {args.workload}: inputs ready", file=sys.stderr, flush=True)
     d = _gpu.to_device(p)
+
+    def step():
+        if replay:
+            _gpu.run_replay(d)
+        else:
+            _gpu.run(d, ahead=args.ahead)
+
     torch.cuda.synchronize()
     for _ in range(args.warmup):
-        _gpu.run(d, ahead=args.ahead)
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -156,7 +189,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         starts[i].record()
-        _gpu.run(d, ahead=args.ahead)
+        step()
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -167,9 +200,13 @@ def main():
           file=sys.stderr, flush=True)
 
     items = p["B"] * p["H"]
-    abytes = algorithmic_bytes(p)
+    abytes = replay_algorithmic_bytes(p) if replay else algorithmic_bytes(p)
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
+    if not replay:
+        extra = {"record": p["record"], "gate_mode": p["gate_mode"]}
+    else:
+        extra = {"tokens_applied": int(p["n"].sum())}
     result = {
         "metric": "KDA decode (request,head)-steps/sec and achieved HBM GB/s (% of peak)",
         "value": items / (ms_per_step * 1e-3),
@@ -183,18 +220,19 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: KDA step T={p['T']}, B={p['B']} requests, "
-                               f"H={p['H']} heads, d=128, {p['N']}-slot FP32 state pool",
-                   "B": p["B"], "H": p["H"], "T": p["T"], "N": p["N"], "items": items,
-                   "record": p["record"], "gate_mode": p["gate_mode"]},
+        "config": {"workload": f"{args.workload}: KDA {'replay' if replay else 'step'} "
+                               f"T={p['T']}, B={p['B']} requests, H={p['H']} heads, d=128, "
+                               f"{p['N']}-slot FP32 state pool",
+                   "B": p["B"], "H": p["H"], "T": p["T"], "N": p["N"], "items": items},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": abytes,
                      "kernel_us": kernel_ms * 1e3},
     }
+    result["config"].update(extra)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(p)
+        result["cpu_baseline"] = cpu_baseline(p, replay=replay)
     print(json.dumps(result))
 
 

@@ -135,6 +135,36 @@ kda_status kda_verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t*
                       int record, int gate_mode, int ahead, void* stream);
 
 /*
+ * kda_replay -- RecoverSSM: the state after the first n accepted tokens of a
+ * record-mode kda_verify, rebuilt from the checkpoint page that verify read
+ * and the records it wrote (the KdaWide class docstring's RecoverSSM mode;
+ * the replay itself is not shown on the page).  Per token t < n[b], with the
+ * step's own operations:
+ *   k_hat = k (sum k^2 + 1e-6)^-1/2      k = rec_kg[b, h, t, 0:128]
+ *   a     = exp(lower_bound * sigmoid(exp(A_log[h]) * (raw_g + dt_bias)))
+ *                                         raw_g = rec_kg[b, h, t, 128:256]
+ *   S[v][key] <- k_hat[key] u[v] + S[v][key] a[key]   u = rec_u[b, h, t, :]
+ *
+ *   rec_u     [B, H, T, 128] FP32, rec_kg [B, H, T, 256] BF16 (as written
+ *             by kda_verify with record; T its token count)
+ *   a_log [H], dt_bias [H*128] FP32; lower_bound as given to kda_verify
+ *   src_slots [B]  checkpoint slot of each request (the slot verify read)
+ *   dst_slots [B]  slot that receives the state after n tokens (may equal
+ *                  the request's own src_slots entry: in place)
+ *   n_tokens  [B]  0 <= n <= T; n = 0 copies the checkpoint
+ *   state     [N, H, 128, 128] FP32
+ * A request whose src or dst lies outside [1, N) or whose n lies outside
+ * [0, T] is skipped (nothing is written for it).  Caller contract: the dst
+ * slots are distinct across requests and no dst is another request's src.
+ * Status: KDA_ERR_TOKENS for T outside [1, 8]; KDA_ERR_SHAPE, KDA_ERR_NULL,
+ * KDA_ERR_LAUNCH as for the other entry points.
+ */
+kda_status kda_replay(const float* rec_u, const uint16_t* rec_kg, const float* a_log,
+                      const float* dt_bias, const int32_t* src_slots, const int32_t* dst_slots,
+                      const int32_t* n_tokens, float* state, float lower_bound, int B, int H,
+                      int N, int T, void* stream);
+
+/*
  * kda_validate -- the host-side checks of kda_verify (T = 1 checks a decode
  * call, with slot_stride and accepted ignored) without enqueuing anything.
  * Touches no device memory and makes no HIP call: usable without a GPU.

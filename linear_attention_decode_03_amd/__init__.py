@@ -6,4 +6,5 @@ libkda.so next to this file.  `kda` is the thin ctypes binding; `inputs`
 makes seeded synthetic operands.  Importing the package loads nothing.
 """
 
-from .kda import kda_decode, kda_status_string, kda_validate, kda_verify, load_library  # noqa: F401
+from .kda import (kda_decode, kda_replay, kda_status_string, kda_validate, kda_verify,  # noqa: F401
+                  load_library)

@@ -43,6 +43,8 @@ def load_library(path: str = LIB_PATH):
         lib.kda_verify.argtypes = _OPERANDS + [_P] * 3 + [_I] * 9 + [_P]
         lib.kda_validate.restype = _I
         lib.kda_validate.argtypes = _OPERANDS + [_P] * 3 + [_I] * 8
+        lib.kda_replay.restype = _I
+        lib.kda_replay.argtypes = [_P] * 8 + [_F] + [_I] * 4 + [_P]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [_I]
         _lib = lib
@@ -172,6 +174,39 @@ def kda_verify(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, 
         _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b), _ptr(accepted),
         _ptr(rec_u), _ptr(rec_kg), B, H, N, W, T, int(slots.shape[1]), int(bool(record)),
         int(gate_mode), int(ahead), _stream(stream))
+    _raise(status)
+
+
+def kda_replay(rec_u, rec_kg, a_log, dt_bias, src_slots, dst_slots, n_tokens, state,
+               lower_bound, stream=None):
+    """RecoverSSM replay: the state after the first n_tokens[b] recorded
+    tokens, rebuilt from the checkpoint pages src_slots into dst_slots; see
+    kda_replay in include/kda.h."""
+    import torch
+
+    if rec_u.dim() != 4:
+        raise ValueError("rec_u: expected [B, H, T, 128]")
+    B, H, T = int(rec_u.shape[0]), int(rec_u.shape[1]), int(rec_u.shape[2])
+    dev = state.device
+    _check("rec_u", rec_u, torch.float32, 4, dev)
+    _check("rec_kg", rec_kg, torch.bfloat16, 4, dev)
+    _check("a_log", a_log, torch.float32, 1, dev)
+    _check("dt_bias", dt_bias, torch.float32, 1, dev)
+    _check("state", state, torch.float32, 4, dev)
+    for name, t in (("src_slots", src_slots), ("dst_slots", dst_slots), ("n_tokens", n_tokens)):
+        _check(name, t, torch.int32, 1, dev)
+        if t.shape[0] != B:
+            raise ValueError(f"{name}: expected [B]")
+    if tuple(rec_u.shape) != (B, H, T, HEAD_DIM) or tuple(rec_kg.shape) != (B, H, T, 2 * HEAD_DIM):
+        raise ValueError("rec_u / rec_kg: expected [B, H, T, 128] / [B, H, T, 256]")
+    if tuple(a_log.shape) != (H,) or tuple(dt_bias.shape) != (H * HEAD_DIM,):
+        raise ValueError("a_log / dt_bias: expected [H] / [H*128]")
+    if state.shape[1] != H or tuple(state.shape[2:]) != (HEAD_DIM, HEAD_DIM):
+        raise ValueError("state: expected [N, H, 128, 128]")
+    status = load_library().kda_replay(
+        _ptr(rec_u), _ptr(rec_kg), _ptr(a_log), _ptr(dt_bias), _ptr(src_slots), _ptr(dst_slots),
+        _ptr(n_tokens), _ptr(state), float(lower_bound), B, H, int(state.shape[0]), T,
+        _stream(stream))
     _raise(status)
 
 

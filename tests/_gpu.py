@@ -46,3 +46,10 @@ def run(d, ahead=-1, stream=None):
         kda.kda_verify(*args, d["accepted"], d.get("rec_u"), d.get("rec_kg"), T=d["T"],
                        record=bool(d["record"]), gate_mode=d["gate_mode"], ahead=ahead,
                        stream=stream)
+
+
+
+def run_replay(d, stream=None):
+    """One replay on the device operands d (to_device of a replay problem)."""
+    kda.kda_replay(d["rec_u"], d["rec_kg"], d["a_log"], d["dt_bias"], d["src"], d["dst"], d["n"],
+                   d["state"], d["lower_bound"], stream=stream)

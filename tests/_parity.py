@@ -164,3 +164,26 @@ def _live_items(p):
         if ok:
             live.extend(b * H + h for h in range(H))
     return np.asarray(live, dtype=np.int64)
+
+
+def compare_replay(before, ref, got_state):
+    """Replay contract: every valid request's dst pages within 1e-4 of the
+    oracle (relative to |r| + rms of the page); every other page keeps its
+    bits.  Returns the worst relative error."""
+    N, H = before["N"], before["H"]
+    valid = [b for b in range(before["B"])
+             if 0 < before["src"][b] < N and 0 < before["dst"][b] < N and 0 <= before["n"][b] <= before["T"]]
+    dst = {int(before["dst"][b]) for b in valid}
+    for s in range(N):
+        if s not in dst:
+            assert np.array_equal(got_state[s].view(np.uint32), before["state"][s].view(np.uint32)), \
+                f"page {s} changed but is no replay target"
+    worst = 0.0
+    for s in dst:
+        r = ref["state"][s].reshape(H, -1).astype(np.float64)
+        g = got_state[s].reshape(H, -1).astype(np.float64)
+        rms = np.sqrt((r * r).mean(axis=1, keepdims=True))
+        m = float((np.abs(g - r) / (np.abs(r) + rms)).max())
+        worst = max(worst, m)
+        assert m <= 1e-4, f"replay page {s}: relative error {m:.3e}"
+    return worst

@@ -33,7 +33,7 @@ def declared():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert names == ["kda_decode", "kda_status_string", "kda_validate", "kda_verify"]
+    assert names == ["kda_decode", "kda_replay", "kda_status_string", "kda_validate", "kda_verify"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -90,6 +90,18 @@ def test_entry_points_reject_before_device_work(lib):
     st = lib.kda_verify(*args, -5.0, 0.088, 1e-6, P(0x1000), P(0x1000), None, None,
                         4, 2, 40, 6, 4, 4, 1, 0, -1, None)
     assert st == NUL  # record without record buffers
+
+
+def test_replay_rejects_before_device_work(lib):
+    P = ctypes.c_void_p
+    ptrs = [P(0x1000)] * 8
+    for T, B, H, N, want in ((0, 4, 2, 9, TOK), (9, 4, 2, 9, TOK), (4, -1, 2, 9, SHP),
+                             (4, 4, 0, 9, SHP), (4, 4, 2, 0, SHP), (4, 0, 2, 9, OK)):
+        assert lib.kda_replay(*ptrs, -5.0, B, H, N, T, None) == want
+    assert lib.kda_replay(*ptrs, float("nan"), 4, 2, 9, 4, None) == SHP
+    nul = list(ptrs)
+    nul[4] = None
+    assert lib.kda_replay(*nul, -5.0, 4, 2, 9, 4, None) == NUL
 
 
 def test_binding_raises_value_error(lib):
