@@ -8,10 +8,13 @@ seeded synthetic inputs resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is (request, head) items per second;
 `roofline` relates the kernel's algorithmic bytes per launch to its average
-duration, measured with HIP events around each launch on the launch stream;
+duration, measured with HIP events around each launch on the launch stream
+(back-to-back launches); `roofline.cold` repeats that with a 1 GiB scratch
+write before each launch, so that no operand is cached;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                    [--cold-launches C]
     python bench.py --mode copy      # 1 GiB device copies (counter calibration)
 
 Workloads: tiny_decode, decode_b64, decode_b256 (default), verify_t4,
@@ -31,7 +34,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_03_amd", "csrc", "kda.hip")
+CSRC = os.path.join(ROOT, "linear_attention_decode_03_amd", "csrc")
+# The sources a workload's kernel is built from: a counter summary taken on
+# other source text does not describe the current kernel.
+KERNEL_SOURCES = {
+    "step": ("kda_device.hpp", "kda_stages.hpp", "kda_step.hip"),
+    "replay": ("kda_device.hpp", "kda_replay.hip"),
+}
+
+
+def kernel_source_hash(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 D = 128
 
 
@@ -86,7 +102,7 @@ def measured_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    src_hash = kernel_source_hash("replay" if workload.startswith("replay") else "step")
     if fields.get("kernel_source_sha256") != src_hash:
         return None
     try:
@@ -146,6 +162,7 @@ def main():
     ap.add_argument("--workload", default="decode_b256")
     ap.add_argument("--ahead", type=int, default=-1)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cold-launches", type=int, default=20)
     ap.add_argument("--mode", choices=["kda", "copy"], default="kda")
     args = ap.parse_args()
 
@@ -199,6 +216,23 @@ def main():
     print(f"[bench] {K} steps, {ms_per_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
+    # Cold launches: a 1 GiB scratch write before each one (outside the
+    # launch's own events) evicts the L2s and the memory-side cache.
+    k_cold = max(0, args.cold_launches)
+    cold = []
+    if k_cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold_s = [torch.cuda.Event(enable_timing=True) for _ in range(k_cold)]
+        cold_e = [torch.cuda.Event(enable_timing=True) for _ in range(k_cold)]
+        for i in range(k_cold):
+            flush.fill_(float(i))
+            cold_s[i].record()
+            step()
+            cold_e[i].record()
+        torch.cuda.synchronize()
+        del flush
+        cold = sorted(s_.elapsed_time(e_) for s_, e_ in zip(cold_s, cold_e))
+
     items = p["B"] * p["H"]
     abytes = replay_algorithmic_bytes(p) if replay else algorithmic_bytes(p)
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
@@ -227,7 +261,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": abytes,
-                     "kernel_us": kernel_ms * 1e3},
+                     "kernel_us": kernel_ms * 1e3,
+                     "cold": None if not cold else {
+                         "kernel_us_median": cold[k_cold // 2] * 1e3, "launches": k_cold,
+                         "achieved": abytes / (cold[k_cold // 2] * 1e-3) / 1e9,
+                         "frac": abytes / (cold[k_cold // 2] * 1e-3) / 1e9 / HBM_PEAK_GBPS}},
     }
     result["config"].update(extra)
     if not args.no_cpu:

@@ -1,6 +1,6 @@
 """MI355X-native Kimi Delta Attention (KDA) decode / verify step.
 
-The computation lives in hand-written HIP kernels for gfx950 (csrc/kda.hip),
+The computation lives in hand-written HIP kernels for gfx950 (csrc/),
 exported through the C ABI declared in include/kda.h and built into
 libkda.so next to this file.  `kda` is the thin ctypes binding; `inputs`
 makes seeded synthetic operands.  Importing the package loads nothing.

@@ -1,6 +1,8 @@
 """Builds the HIP library (libkda.so) in-tree for gfx950.
 
-The library is one translation unit, csrc/kda.hip, compiled with hipcc.
+The library is built by one hipcc call from the kernel sources in csrc/
+(kda_step.hip: decode, verify and record mode; kda_replay.hip: the replay;
+the headers kda_device.hpp and kda_stages.hpp hold the shared device code).
 Packed FP32 instructions are switched off (-packed-fp32-ops): the kernels
 are written for scalar FP32 FMAs.
 """
@@ -12,7 +14,8 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "kda.hip")
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, f) for f in ("kda_step.hip", "kda_replay.hip")]
 LIB = os.path.join(HERE, "libkda.so")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,11 +26,11 @@ def hipcc_command(out: str = LIB) -> list:
     return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-command-line-argument",
-            f"-I{INCLUDE}", "-o", out, SRC]
+            f"-I{INCLUDE}", f"-I{CSRC}", "-o", out, *SOURCES]
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compiles csrc/kda.hip into libkda.so next to this file (atomically)."""
+    """Compiles the csrc/ sources into libkda.so next to this file (atomically)."""
     tmp = LIB + ".tmp"
     r = subprocess.run(hipcc_command(tmp), capture_output=True, text=True)
     if r.returncode != 0:

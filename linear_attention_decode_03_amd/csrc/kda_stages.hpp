@@ -1,0 +1,412 @@
+// The stages of one KDA step item shared by the step kernels: operands,
+// slot resolution and padding, the prologue (causal convolution + SiLU,
+// L2 norms, beta, gate projection, decay) and the epilogue (gated RMSNorm).
+//
+// Operation: the KdaWide kernel body of the vLLM API page
+// vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.wide; the
+// argument contract is in include/kda.h.
+#ifndef KDA_STAGES_HPP
+#define KDA_STAGES_HPP
+
+#include "kda_device.hpp"
+
+namespace {
+
+struct Args {
+  const uint16_t* x;
+  const uint16_t* conv_w;
+  const uint16_t* conv_b;
+  uint16_t* conv_state;
+  const uint16_t* f_a;
+  const uint16_t* beta;
+  const float* a_log;
+  const float* dt_bias;
+  const int32_t* slots;
+  float* state;
+  uint16_t* out;
+  const uint16_t* gate;
+  const uint16_t* norm_w;
+  const uint16_t* f_b;
+  const int32_t* accepted;
+  float* rec_u;
+  uint16_t* rec_kg;
+  float lower_bound, scale, eps;
+  int B, H, N, W, slot_stride;
+  int ahead;  // prefetch distance in items (0: off), a multiple of 8
+};
+
+// ---- shared memory -----------------------------------------------------------
+
+// Per-item tables.  q, k, a and g are dead once the inputs are reduced to
+// what the body needs; the record-mode body reuses their space for P, C and o.
+template <int T>
+struct Inputs {
+  float q[T][kD], k[T][kD], a[T][kD];
+  float g[T][kD];  // FP32 gate projection before BF16 rounding
+};
+template <int T>
+struct RecordOut {
+  float P[16][kD];  // S0 W
+  float C[16][16];  // W X^T
+  float o[T][kD];
+};
+template <int T, bool kRecordBody>
+struct Shared {
+  union {
+    Inputs<T> in;
+    RecordOut<T> out;
+  } u;
+  float v[T][kD];
+  float o[kRecordBody ? 1 : T][kD];  // token-by-token body's outputs
+  float beta[kMaxT];
+  float sq[T][2][2];  // [token][q, k][wave 0, 1]
+  float os[T][2];     // [token][wave 0, 1]
+};
+
+// Record-mode operand tables: W rows A_t k_hat_t (t < T) and A_t q_hat_t
+// (T + t), X rows k_hat_t / A_t; rows beyond are zero.
+constexpr int kPad = kD + 4;  // W row pitch: the 16 rows read together fall in different banks
+struct RecordTables {
+  float W[16][kPad];
+  float X[16][kD];
+};
+
+// ---- item resolution -----------------------------------------------------
+
+struct Item {
+  int b, h, rs, cs, off;
+  size_t token0;
+  int dim;
+};
+
+// Slot resolution (uniform over the workgroup); false means padding.
+template <int T>
+__device__ __forceinline__ bool resolve(const Args& A, Item& it) {
+  const int H = A.H;
+  it.h = blockIdx.x % H;
+  it.b = blockIdx.x / H;
+  it.dim = H * kD;
+  it.token0 = static_cast<size_t>(it.b) * T;
+  it.off = 0;
+  if constexpr (T == 1) {
+    it.rs = A.slots[it.b];
+    it.cs = it.rs;
+    return it.rs > 0 && it.rs < A.N;
+  } else {
+    const int acc = A.accepted[it.b];
+    const int lim = T < A.slot_stride ? T : A.slot_stride;
+    it.rs = 0;
+    it.cs = 0;
+    if (acc < 1 || acc > lim) return false;
+    it.off = acc - 1;
+    it.rs = A.slots[static_cast<size_t>(it.b) * A.slot_stride + it.off];
+    it.cs = A.slots[static_cast<size_t>(it.b) * A.slot_stride];
+    return it.rs > 0 && it.rs < A.N && it.cs >= 0 && it.cs < A.N;
+  }
+}
+
+// Prefetch (the page's prefetch_next): touch every 128-byte line of the
+// state page that item blockIdx + ahead will read, so that it is on its way
+// into the L2 of the XCD that runs that item (workgroups go round-robin to
+// the 8 XCDs; ahead is a multiple of 8) and into the memory-side cache.  Two
+// 4-byte loads per thread with the default cache policy (so the lines are
+// kept), issued after the item's own page loads so that the in-order
+// retirement of loads does not hold up the input phase; the values are only
+// kept alive by a test that is never true at run time.  Measured on MI355X
+// this never pays: at 8 MiB of pages in flight per XCD against a 4 MB L2 the
+// touched lines are mostly gone before use, so it adds reads (decode B=256:
+// +5 % at ahead 256, +28 % at 1024); the default is off.
+template <int T>
+__device__ __forceinline__ void prefetch_page(const Args& A, float& sink) {
+  sink = 0.0f;
+  const int item = static_cast<int>(blockIdx.x) + A.ahead;
+  if (A.ahead <= 0 || item >= static_cast<int>(gridDim.x)) return;
+  const int b = item / A.H, h = item % A.H;
+  int slot;
+  if constexpr (T == 1) {
+    slot = A.slots[b];
+  } else {
+    const int acc = A.accepted[b];
+    const int lim = T < A.slot_stride ? T : A.slot_stride;
+    if (acc < 1 || acc > lim) return;
+    slot = A.slots[static_cast<size_t>(b) * A.slot_stride + acc - 1];
+  }
+  if (slot <= 0 || slot >= A.N) return;
+  const float* page = A.state + (static_cast<size_t>(slot) * A.H + h) * (kD * kD);
+  const int line = 64 * static_cast<int>(threadIdx.x);  // floats: 256 B per thread
+  sink = page[line] + page[line + 32];
+}
+
+__device__ __forceinline__ void keep_alive(const Args& A, float sink) {
+  if (A.B < 0 && sink == 0.0f) A.out[0] = 0;  // B < 0 never reaches a kernel
+}
+
+template <int T>
+__device__ __forceinline__ void write_padding(const Args& A, const Item& it) {
+  const int tid = threadIdx.x;
+  if (tid < kD) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      A.out[(it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + tid] = 0;
+  }
+}
+
+// Output-gate logits and norm weight of channel tid (threads 0-127), loaded
+// at the start so that the last phase does not wait on memory.
+template <int T>
+struct OutputOperands {
+  uint16_t gate[T];
+  float nw;
+};
+
+template <int T>
+__device__ __forceinline__ void load_output_operands(const Args& A, const Item& it,
+                                                     OutputOperands<T>& oo) {
+  const int tid = threadIdx.x;
+  if (tid < kD) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      oo.gate[t] = A.gate[(it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + tid];
+    oo.nw = bf16_bits_to_f32(A.norm_w[tid]);
+  }
+}
+
+// ---- prologue: convolution, SiLU, norms, gate projection, decay -------------
+
+// Convolution + SiLU.  Threads 0-127 make q and k of channel tid, threads
+// 128-255 make v of channel tid - 128.  Split in two so that the operand
+// loads can be issued before the state page: loads of a wave retire in issue
+// order, so inputs loaded after the page could not be used before all of it
+// has arrived.
+template <int T>
+struct ConvOperands {
+  uint16_t raw[2][3 + T];  // [part slot][tap0, tap1, tap2, x_0 .. x_{T-1}]
+  float w[2][4];
+  float bias[2];
+};
+
+template <int T, bool kBias>
+__device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOperands<T>& co) {
+  const int tid = threadIdx.x;
+  const int c = tid & (kD - 1);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (s == 1 && tid >= kD) break;
+    const int part = tid < kD ? s : 2;
+    const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
+    const uint16_t* col = A.conv_state + (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) co.raw[s][i] = col[it.off + i];
+#pragma unroll
+    for (int t = 0; t < T; ++t) co.raw[s][3 + t] = A.x[(it.token0 + t) * 3 * it.dim + ch];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      co.w[s][i] = bf16_bits_to_f32(A.conv_w[(static_cast<size_t>(part) * 4 + i) * it.dim +
+                                             static_cast<size_t>(it.h) * kD + c]);
+    co.bias[s] = kBias ? bf16_bits_to_f32(A.conv_b[ch]) : 0.0f;
+  }
+}
+
+// The window is rewritten in place after it was read: [tap1, tap2, x_0 ..];
+// record mode stores k.
+template <int T, bool kRecord, class SH>
+__device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& sh,
+                                             const ConvOperands<T>& co) {
+  const int tid = threadIdx.x;
+  const int c = tid & (kD - 1);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (s == 1 && tid >= kD) break;
+    const int part = tid < kD ? s : 2;
+    const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
+    uint16_t* col = A.conv_state + (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
+    col[0] = co.raw[s][1];
+    col[1] = co.raw[s][2];
+#pragma unroll
+    for (int t = 0; t < T; ++t) col[2 + t] = co.raw[s][3 + t];
+    float* dst = part == 0 ? &sh.u.in.q[0][0] : part == 1 ? &sh.u.in.k[0][0] : &sh.v[0][0];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float acc = co.bias[s];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(bf16_bits_to_f32(co.raw[s][t + i]), co.w[s][i], acc);
+      const float y = silu_bf16(acc);
+      dst[t * kD + c] = y;
+      if constexpr (kRecord) {
+        if (part == 1)
+          A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + c] =
+              static_cast<uint16_t>(f32_to_bf16_bits(y));
+      }
+    }
+  }
+}
+
+template <int T, bool kRecord, bool kBias, class SH>
+__device__ __forceinline__ void conv_silu(const Args& A, const Item& it, SH& sh) {
+  ConvOperands<T> co;
+  conv_load<T, kBias>(A, it, co);
+  conv_compute<T, kRecord>(A, it, sh, co);
+}
+
+// Sums of squares of q and k (waves 0 and 1 hold channels 0-63, 64-127) and
+// beta = sigmoid(logit).
+template <int T, class SH>
+__device__ __forceinline__ void norms_beta(const Args& A, const Item& it, SH& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (wave < 2) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float q = sh.u.in.q[t][tid], k = sh.u.in.k[t][tid];
+      const float sq = wave_sum(q * q), sk = wave_sum(k * k);
+      if (lane == 0) {
+        sh.sq[t][0][wave] = sq;
+        sh.sq[t][1][wave] = sk;
+      }
+    }
+  }
+  if (tid < T)
+    sh.beta[tid] = sigmoid_f32(bf16_bits_to_f32(A.beta[(it.token0 + tid) * A.H + it.h]));
+}
+
+// Gate projection raw_g[t][f] = BF16(sum_j F_B[h*128+f][j] f_a[t][j]), exact:
+// the products of two BF16 values are exact and are summed in FP64.
+// One token (decode): on the vector ALUs.  Thread holds features
+// 16i + (tid >> 4) and columns 8(tid & 15) .. +7 (every 16-byte load of the
+// workgroup contiguous); a feature's 16 partial sums sit in one 16-lane row.
+struct GateOperands {
+  uint4 fb[8];
+  uint4 fa;
+};
+
+__device__ __forceinline__ void gate_load(const Args& A, const Item& it, GateOperands& go) {
+  const int tid = threadIdx.x;
+  const int fsub = tid >> 4;
+  const int j0 = 8 * (tid & 15);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    go.fb[i] = *reinterpret_cast<const uint4*>(
+        A.f_b + (static_cast<size_t>(it.h) * kD + 16 * i + fsub) * kD + j0);
+  go.fa = *reinterpret_cast<const uint4*>(A.f_a + it.token0 * kD + j0);
+}
+
+template <class SH>
+__device__ __forceinline__ void gate_valu(const GateOperands& go, SH& sh) {
+  const int tid = threadIdx.x;
+  const int fsub = tid >> 4;
+  const uint4 fa4 = go.fa;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 fb = go.fb[i];
+    double acc = static_cast<double>(bf16_lo(fb.x) * bf16_lo(fa4.x));
+    acc += static_cast<double>(bf16_hi(fb.x) * bf16_hi(fa4.x));
+    acc += static_cast<double>(bf16_lo(fb.y) * bf16_lo(fa4.y));
+    acc += static_cast<double>(bf16_hi(fb.y) * bf16_hi(fa4.y));
+    acc += static_cast<double>(bf16_lo(fb.z) * bf16_lo(fa4.z));
+    acc += static_cast<double>(bf16_hi(fb.z) * bf16_hi(fa4.z));
+    acc += static_cast<double>(bf16_lo(fb.w) * bf16_lo(fa4.w));
+    acc += static_cast<double>(bf16_hi(fb.w) * bf16_hi(fa4.w));
+    acc = row_sum16_f64(acc);
+    if ((tid & 15) == 0) sh.u.in.g[0][16 * i + fsub] = static_cast<float>(acc);
+  }
+}
+
+// Several tokens: FP64 MFMA 16x16x4, D[feature][token] over K = 128 columns
+// (tokens >= T are zero columns).  Wave w computes feature tiles 32w and
+// 32w + 16.  Lane (g = l >> 4, c = l & 15) feeds A[c][g] = F_B[f0 + c][k] and
+// B[g][c] = f_a[token c][k] with k = 32q + 8g + e at step (q, e): each lane's
+// operands are 16-byte loads; the 128 columns are visited in that order.  D layout of this instruction: lane l,
+// element r holds D[l/16 + 4r][l%16].
+template <int T, class SH>
+__device__ __forceinline__ void gate_mfma(const Args& A, const Item& it, SH& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll 1
+  for (int tile = 0; tile < 2; ++tile) {
+    const int f0 = 32 * wave + 16 * tile;
+    // Two independent accumulation chains (even and odd 32-column quarters);
+    // the sums are exact in FP64, so the chain structure does not change a bit.
+    f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+#pragma unroll 1
+    for (int q0 = 0; q0 < 4; q0 += 2) {
+      uint4 fb[2], fa[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int q = q0 + j;
+        fb[j] = *reinterpret_cast<const uint4*>(
+            A.f_b + (static_cast<size_t>(it.h) * kD + f0 + c) * kD + 32 * q + 8 * g);
+        fa[j] = make_uint4(0, 0, 0, 0);
+        if (c < T)
+          fa[j] = *reinterpret_cast<const uint4*>(A.f_a + (it.token0 + c) * kD + 32 * q + 8 * g);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(bf16_at(fb[j], e)),
+                                                         static_cast<double>(bf16_at(fa[j], e)),
+                                                         acc[j], 0, 0, 0);
+    }
+    if (c < T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sh.u.in.g[c][f0 + g + 4 * r] = static_cast<float>(acc[0][r] + acc[1][r]);
+    }
+  }
+}
+
+// Raw gate to BF16, then the decay of key channel f = tid (threads 0-127);
+// record mode stores raw_g.
+template <int T, bool kRecord, class SH>
+__device__ __forceinline__ void decay(const Args& A, const Item& it, SH& sh) {
+  const int tid = threadIdx.x;
+  if (tid < kD) {
+    const float e = expf(A.a_log[it.h]);
+    const float dt = A.dt_bias[static_cast<size_t>(it.h) * kD + tid];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float raw_g = round_bf16(sh.u.in.g[t][tid]);
+      sh.u.in.a[t][tid] = decay_f32(e, raw_g, dt, A.lower_bound);
+      if constexpr (kRecord)
+        A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + kD + tid] =
+            static_cast<uint16_t>(f32_to_bf16_bits(raw_g));
+    }
+  }
+}
+
+template <int T, class SH>
+__device__ __forceinline__ void norm_factors(const SH& sh, int t, float& fq, float& fk) {
+  fq = 1.0f / sqrtf((sh.sq[t][0][0] + sh.sq[t][0][1]) + 1.0e-6f);
+  fk = 1.0f / sqrtf((sh.sq[t][1][0] + sh.sq[t][1][1]) + 1.0e-6f);
+}
+
+// ---- epilogue: gated RMSNorm --------------------------------------------------
+
+template <int T, class SH>
+__device__ __forceinline__ void gated_rmsnorm(const Args& A, const Item& it, SH& sh,
+                                              const float (*o)[kD],
+                                              const OutputOperands<T>& oo) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (wave < 2) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float ot = o[t][tid];
+      const float ss = wave_sum(ot * ot);
+      if (lane == 0) sh.os[t][wave] = ss;
+    }
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float variance = (sh.os[t][0] + sh.os[t][1]) * (1.0f / 128.0f) + A.eps;
+      const float rstd = 1.0f / sqrtf(variance);
+      const float sg = sigmoid_f32(bf16_bits_to_f32(oo.gate[t]));
+      const size_t idx = (it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + tid;
+      A.out[idx] = static_cast<uint16_t>(f32_to_bf16_bits(((o[t][tid] * rstd) * oo.nw) * sg));
+    }
+  }
+}
+
+}  // namespace
+
+#endif  // KDA_STAGES_HPP

@@ -1,0 +1,435 @@
+// KDA decode / verify step for MI355X (gfx950, CDNA4): the step kernels and
+// the C ABI of kda_decode, kda_verify and kda_validate.
+//
+// Operation: the KdaWide step of the vLLM API page
+// vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.kda.wide (class
+// docstring, constructor, kernel body, helpers silu / decay); the argument
+// contract is in include/kda.h.
+//
+// Design (one workgroup of 4 wave64s per (request, head) item):
+//  * The item's 128x128 FP32 state page (64 KiB) lives in VGPRs for every
+//    token of the step: thread (wave w, lane l) owns value rows
+//    32(l >> 4) + 8w + i, i < 8, and keys 4(l & 15) + [0, 4) and
+//    64 + 4(l & 15) + [0, 4): 64 floats.  Each 16-byte load or store of a
+//    wave covers four 256-byte row segments 16 KiB apart, so every HBM line
+//    is used whole and each instruction spreads over more channels.  The
+//    loads are issued after the input loads and land while the inputs are
+//    prepared.
+//  * A row's 128 keys sit in one 16-lane DPP row, so the two row reductions
+//    per token (S.k and S.q) are four DPP adds each, with no LDS traffic.
+//  * The BF16 rounding points that feed the state (SiLU outputs and the raw
+//    gate) are the correctly rounded values of the page's FP32 operations:
+//    the SiLU takes a fast FP32 path whose error bound decides the BF16
+//    value unless it lies near a rounding midpoint (then exp is evaluated in
+//    FP64), and the gate projection (products of BF16 values, exact in FP64)
+//    is accumulated in FP64 and rounded once.  Only the recurrence's dot
+//    products keep an FP32 reduction order of their own.
+//  * Record mode (no state written) runs in closed form on FP32 MFMA from
+//    one pass over the page read.
+//  * Items are numbered head-fastest; with H a multiple of 8 the
+//    round-robin dispatch over the 8 XCDs sends every head to one XCD, so
+//    each XCD's L2 keeps only its heads' 32 KiB F_B blocks.
+#include "kda.h"
+#include "kda_stages.hpp"
+
+namespace {
+
+// ---- decode / verify: the recurrence token by token ------------------------
+
+// Thread (wave w, lane l) owns rows 32(l >> 4) + 8w + i (i < 8) and keys
+// 4(l & 15) + [0, 4) and 64 + 4(l & 15) + [0, 4): 64 floats in VGPRs.  Every
+// 16-byte access of a wave covers four 256-byte row segments 16 KiB apart,
+// which spreads each instruction over more HBM channels; a row's keys sit in
+// one 16-lane DPP row.
+template <int T, bool kRecord, bool kBias>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void kda_step_kernel(const Args A) {
+  Item it;
+  if (!resolve<T>(A, it)) {  // padding: BF16 zeros, nothing else touched
+    write_padding<T>(A, it);
+    return;
+  }
+  __shared__ Shared<T, false> sh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15;
+  const int row0 = 32 * (lane >> 4) + 8 * wave;
+  const int lane_off = (row0 * kD + 4 * c16) * 4;
+
+  // 1. Input operands first, then the state page (one buffer resource per
+  //    64 KiB page): the inputs are used while the page is still arriving.
+  ConvOperands<T> co;
+  conv_load<T, kBias>(A, it, co);
+  GateOperands go;
+  if constexpr (T == 1) gate_load(A, it, go);
+  OutputOperands<T> oo;
+  float4 st[8][2];
+  {
+    const __amdgpu_buffer_rsrc_t page = page_rsrc(A.state, it.rs, it.h, A.H);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) st[i][j] = load_f4(page, lane_off, i * kD * 4 + j * 256);
+  }
+  float sink;
+  prefetch_page<T>(A, sink);
+
+  // 2. Inputs.
+  conv_compute<T, kRecord>(A, it, sh, co);
+  norms_beta<T>(A, it, sh);
+  if constexpr (T == 1) gate_valu(go, sh); else gate_mfma<T>(A, it, sh);
+  __syncthreads();
+  decay<T, kRecord>(A, it, sh);
+  __syncthreads();
+
+  // 3. The recurrence, token by token.
+#pragma unroll 1
+  for (int t = 0; t < T; ++t) {
+    float fq, fk;
+    norm_factors<T>(sh, t, fq, fk);
+    float kh[8], qh[8], a[8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&sh.u.in.k[t][64 * j + 4 * c16]);
+      const float4 q4 = *reinterpret_cast<const float4*>(&sh.u.in.q[t][64 * j + 4 * c16]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&sh.u.in.a[t][64 * j + 4 * c16]);
+      kh[4 * j + 0] = k4.x * fk; kh[4 * j + 1] = k4.y * fk;
+      kh[4 * j + 2] = k4.z * fk; kh[4 * j + 3] = k4.w * fk;
+      qh[4 * j + 0] = (q4.x * fq) * A.scale; qh[4 * j + 1] = (q4.y * fq) * A.scale;
+      qh[4 * j + 2] = (q4.z * fq) * A.scale; qh[4 * j + 3] = (q4.w * fq) * A.scale;
+      a[4 * j + 0] = a4.x; a[4 * j + 1] = a4.y; a[4 * j + 2] = a4.z; a[4 * j + 3] = a4.w;
+    }
+    const float beta = sh.beta[t];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float* s = reinterpret_cast<float*>(&st[i][0]);  // 8 contiguous floats
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s[e] = s[e] * a[e];
+        dot = fmaf(s[e], kh[e], dot);
+      }
+      dot = row_sum16(dot);
+      const int v = row0 + i;
+      const float u = (sh.v[t][v] - dot) * beta;
+      float o = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s[e] = fmaf(kh[e], u, s[e]);
+        o = fmaf(s[e], qh[e], o);
+      }
+      o = row_sum16(o);
+      if (c16 == 0) {
+        sh.o[t][v] = round_bf16(o);
+        if constexpr (kRecord)
+          A.rec_u[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * kD + v] = u;
+      }
+    }
+    if constexpr (!kRecord) {
+      const int target = T == 1 ? it.rs : A.slots[static_cast<size_t>(it.b) * A.slot_stride + t];
+      if (target > 0 && target < A.N) {
+        float* page = page_ptr(A.state, target, it.h, A.H);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) store_f4(page, lane_off + i * kD * 4 + j * 256, st[i][j]);
+      }
+    }
+  }
+  load_output_operands<T>(A, it, oo);
+  __syncthreads();
+
+  // 4. Gated RMSNorm.
+  gated_rmsnorm<T>(A, it, sh, sh.o, oo);
+  keep_alive(A, sink);
+}
+
+// ---- record mode (RecoverSSM verify): all tokens from one pass over S0 -------
+//
+// With no state to store, the outputs and records follow from the page read,
+// S0, in closed form.  Let A_t be the running product of the decays
+// a_1 ... a_t (per key).  Then S_t = diag(A_t) (S0 + sum_{s<=t} (k_s / A_s) u_s^T)
+// and, per value row v,
+//   u_t = beta_t (v_t - P[t] - sum_{s<t} C[t][s] u_s),
+//   o_t = P[T + t] + sum_{s<=t} C[T + t][s] u_s,
+// with W_t = A_t (.) k_t, W_{T+t} = A_t (.) q_t, X_s = k_s / A_s,
+// P[m][v] = sum_key S0[v][key] W_m[key] and C[m][s] = W_m . X_s.
+// P is a 128 x 128 x 2T contraction and C a 2T x T x 128 one: both run on
+// FP32 MFMA 16x16x4; the state page is loaded straight into the B operand
+// layout (lane (g, c) of wave w holds rows 32w + 16 tile + c, keys
+// 16q + 4g + [0, 4)).  Used when |lower_bound| <= 10, so that every A_t and
+// 1 / A_t stays a normal FP32 number (|log A_t| <= 80).
+template <int T, bool kBias>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void kda_record_kernel(const Args A) {
+  Item it;
+  if (!resolve<T>(A, it)) {
+    write_padding<T>(A, it);
+    return;
+  }
+  __shared__ Shared<T, true> sh;
+  __shared__ RecordTables rt;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+
+  // 1. S0 into the MFMA B-operand layout: [tile][q] = rows 32w + 16 tile + c,
+  //    keys 16q + 4g .. +3 (each instruction: 16 rows x 64 contiguous bytes).
+  float4 st[2][8];
+  {
+    const __amdgpu_buffer_rsrc_t page = page_rsrc(A.state, it.rs, it.h, A.H);
+    const int voff = (32 * wave + c) * kD * 4 + 16 * g;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st[tile][q] = load_f4(page, voff, tile * 16 * kD * 4 + 64 * q);
+  }
+  float sink;
+  prefetch_page<T>(A, sink);
+
+  // 2. Inputs.
+  conv_silu<T, true, kBias>(A, it, sh);
+  norms_beta<T>(A, it, sh);
+  gate_mfma<T>(A, it, sh);
+  __syncthreads();
+  decay<T, true>(A, it, sh);
+  __syncthreads();
+
+  // 3. W and X (thread = key channel), zero rows beyond 2T and T.
+  if (tid < kD) {
+    const int key = tid;
+    float acc = 1.0f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float fq, fk;
+      norm_factors<T>(sh, t, fq, fk);
+      acc = acc * sh.u.in.a[t][key];
+      const float kh = sh.u.in.k[t][key] * fk;
+      const float qh = (sh.u.in.q[t][key] * fq) * A.scale;
+      rt.W[t][key] = acc * kh;
+      rt.W[T + t][key] = acc * qh;
+      rt.X[t][key] = kh / acc;
+    }
+#pragma unroll
+    for (int m = 2 * T; m < 16; ++m) rt.W[m][key] = 0.0f;
+#pragma unroll
+    for (int m = T; m < 16; ++m) rt.X[m][key] = 0.0f;
+  }
+  __syncthreads();  // from here q, k, a and g are dead: P, C and o take their space
+  OutputOperands<T> oo;
+  load_output_operands<T>(A, it, oo);
+
+  // 4. P = S0 W (two 16-row tiles per wave) and, on wave 0, C = W X^T.
+  //    A operand lane (g, c): W[c][16q + 4g + e]; the K order is shared by
+  //    both operands of each product.
+  {
+    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&rt.W[c][16 * q + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[0][q], e), p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[1][q], e), p1, 0, 0, 0);
+      }
+    }
+    // D layout (f32 16x16x4): lane l, element r holds D[4(l/16) + r][l%16].
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sh.u.out.P[4 * g + r][32 * wave + c] = p0[r];
+      sh.u.out.P[4 * g + r][32 * wave + 16 + c] = p1[r];
+    }
+    if (wave == 0) {
+      f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&rt.W[c][16 * q + 4 * g]);
+        const float4 x4 = *reinterpret_cast<const float4*>(&rt.X[c][16 * q + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cc = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(x4, e), cc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh.u.out.C[4 * g + r][c] = cc[r];
+    }
+  }
+  __syncthreads();
+
+  // 5. Per value row v = tid (threads 0-127): the triangular solve for u and o.
+  if (tid < kD) {
+    const int v = tid;
+    float u[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float dot = sh.u.out.P[t][v];
+#pragma unroll
+      for (int s = 0; s < t; ++s) dot = fmaf(sh.u.out.C[t][s], u[s], dot);
+      u[t] = (sh.v[t][v] - dot) * sh.beta[t];
+      float o = sh.u.out.P[T + t][v];
+#pragma unroll
+      for (int s = 0; s <= t; ++s) o = fmaf(sh.u.out.C[T + t][s], u[s], o);
+      sh.u.out.o[t][v] = round_bf16(o);
+      A.rec_u[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * kD + v] = u[t];
+    }
+  }
+  __syncthreads();
+
+  // 6. Gated RMSNorm.
+  gated_rmsnorm<T>(A, it, sh, sh.u.out.o, oo);
+  keep_alive(A, sink);
+}
+
+// ---- host side -------------------------------------------------------------
+
+kda_status check(const Args& A, int T, int record, int gate_mode) {
+  if (T < 1 || T > kMaxT) return KDA_ERR_TOKENS;
+  if (gate_mode != 0 && gate_mode != 1) return KDA_ERR_GATE_MODE;
+  if (record && T == 1) return KDA_ERR_RECORD_T1;
+  if (A.B < 0 || A.H < 1 || A.N < 1) return KDA_ERR_SHAPE;
+  if (A.W < (T == 1 ? 3 : T + 2)) return KDA_ERR_SHAPE;
+  if (T > 1 && A.slot_stride < T) return KDA_ERR_SHAPE;
+  if (!isfinite(A.lower_bound) || !isfinite(A.scale) || !isfinite(A.eps)) return KDA_ERR_SHAPE;
+  // Grid and 32-bit index limits: B*H workgroups; H*128 channels per row.
+  if (static_cast<long long>(A.B) * A.H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+  if (static_cast<long long>(A.H) * 3 * kD * (T + 3) > 0x7fffffffLL) return KDA_ERR_SHAPE;
+  if (A.B == 0) return KDA_OK;
+  if (!A.x || !A.conv_w || !A.conv_state || !A.f_a || !A.beta || !A.a_log || !A.dt_bias ||
+      !A.slots || !A.state || !A.out || !A.gate || !A.norm_w || !A.f_b)
+    return KDA_ERR_NULL;
+  if (T > 1 && !A.accepted) return KDA_ERR_NULL;
+  if (record && (!A.rec_u || !A.rec_kg)) return KDA_ERR_NULL;
+  return KDA_OK;
+}
+
+// Record mode takes the closed-form kernel when the running decay products
+// stay normal FP32 numbers (|lower_bound| <= 10, at most 8 tokens: |log A_t| <= 80).
+constexpr float kRecordBound = 10.0f;
+
+template <int T, bool kRecord>
+kda_status launch_t(const Args& A, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(A.B * A.H));
+  const dim3 block(kThreads);
+  const bool bias = A.conv_b != nullptr;
+  if constexpr (kRecord && T > 1) {
+    if (fabsf(A.lower_bound) <= kRecordBound) {
+      if (bias)
+        hipLaunchKernelGGL((kda_record_kernel<T, true>), grid, block, 0, stream, A);
+      else
+        hipLaunchKernelGGL((kda_record_kernel<T, false>), grid, block, 0, stream, A);
+      return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    }
+  }
+  if (bias)
+    hipLaunchKernelGGL((kda_step_kernel<T, kRecord, true>), grid, block, 0, stream, A);
+  else
+    hipLaunchKernelGGL((kda_step_kernel<T, kRecord, false>), grid, block, 0, stream, A);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <bool kRecord>
+kda_status launch(const Args& A, int T, hipStream_t stream) {
+  switch (T) {
+    case 1: if constexpr (!kRecord) return launch_t<1, false>(A, stream); else return KDA_ERR_RECORD_T1;
+    case 2: return launch_t<2, kRecord>(A, stream);
+    case 3: return launch_t<3, kRecord>(A, stream);
+    case 4: return launch_t<4, kRecord>(A, stream);
+    case 5: return launch_t<5, kRecord>(A, stream);
+    case 6: return launch_t<6, kRecord>(A, stream);
+    case 7: return launch_t<7, kRecord>(A, stream);
+    case 8: return launch_t<8, kRecord>(A, stream);
+    default: return KDA_ERR_TOKENS;
+  }
+}
+
+// The prefetch distance: -1 takes the library default (off: the step is at
+// its measured HBM ceiling without it), other values are rounded up to a
+// multiple of 8 so that the prefetching workgroup and the one that reads the
+// page sit on the same XCD.
+constexpr int kDefaultAhead = 0;
+
+int resolve_ahead(int ahead) {
+  if (ahead < 0) ahead = kDefaultAhead;
+  return (ahead + 7) & ~7;
+}
+
+Args pack(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+          uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta, const float* a_log,
+          const float* dt_bias, const int32_t* slots, float* state, uint16_t* out,
+          const uint16_t* gate, const uint16_t* norm_w, float lower_bound, float scale,
+          float eps, const uint16_t* f_b, const int32_t* accepted, float* rec_u,
+          uint16_t* rec_kg, int B, int H, int N, int W, int slot_stride, int ahead) {
+  Args A;
+  A.x = x; A.conv_w = conv_w; A.conv_b = conv_b; A.conv_state = conv_state; A.f_a = f_a;
+  A.beta = beta; A.a_log = a_log; A.dt_bias = dt_bias; A.slots = slots; A.state = state;
+  A.out = out; A.gate = gate; A.norm_w = norm_w; A.f_b = f_b; A.accepted = accepted;
+  A.rec_u = rec_u; A.rec_kg = rec_kg;
+  A.lower_bound = lower_bound; A.scale = scale; A.eps = eps;
+  A.B = B; A.H = H; A.N = N; A.W = W; A.slot_stride = slot_stride;
+  A.ahead = resolve_ahead(ahead);
+  return A;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_validate(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                        uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                        const float* a_log, const float* dt_bias, const int32_t* slots,
+                        float* state, uint16_t* out, const uint16_t* gate,
+                        const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                        const uint16_t* f_b, const int32_t* accepted, float* rec_u,
+                        uint16_t* rec_kg, int B, int H, int N, int W, int T, int slot_stride,
+                        int record, int gate_mode) {
+  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                      out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg,
+                      B, H, N, W, T == 1 ? 1 : slot_stride, 0);
+  return check(A, T, record, gate_mode);
+}
+
+kda_status kda_decode(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                      uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                      const float* a_log, const float* dt_bias, const int32_t* slots,
+                      float* state, uint16_t* out, const uint16_t* gate,
+                      const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                      const uint16_t* f_b, int B, int H, int N, int W, int gate_mode, int ahead,
+                      void* stream) {
+  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                      out, gate, norm_w, lower_bound, scale, eps, f_b, nullptr, nullptr,
+                      nullptr, B, H, N, W, 1, ahead);
+  const kda_status s = check(A, 1, 0, gate_mode);
+  if (s != KDA_OK || B == 0) return s;
+  return launch<false>(A, 1, static_cast<hipStream_t>(stream));
+}
+
+kda_status kda_verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                      uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                      const float* a_log, const float* dt_bias, const int32_t* slots,
+                      float* state, uint16_t* out, const uint16_t* gate,
+                      const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                      const uint16_t* f_b, const int32_t* accepted, float* rec_u,
+                      uint16_t* rec_kg, int B, int H, int N, int W, int T, int slot_stride,
+                      int record, int gate_mode, int ahead, void* stream) {
+  if (T == 1) return KDA_ERR_TOKENS;  // a one-token step is kda_decode
+  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                      out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg,
+                      B, H, N, W, slot_stride, ahead);
+  const kda_status s = check(A, T, record, gate_mode);
+  if (s != KDA_OK || B == 0) return s;
+  return record ? launch<true>(A, T, static_cast<hipStream_t>(stream))
+                : launch<false>(A, T, static_cast<hipStream_t>(stream));
+}
+
+
+const char* kda_status_string(kda_status status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_TOKENS: return "tokens per request must be in [1, 8] (verify: [2, 8])";
+    case KDA_ERR_GATE_MODE: return "gate_mode must be 0 or 1";
+    case KDA_ERR_RECORD_T1: return "record mode needs more than one token";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "invalid sizes or scalars";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
