@@ -155,20 +155,20 @@ __device__ __forceinline__ void write_padding(const Args& A, const Item& it) {
 // at the start so that the last phase does not wait on memory.
 template <int T>
 struct OutputOperands {
-  uint16_t gate[T];
+  uint32_t gate[T];  // BF16 bits, one per register: packing would consume the load
   float nw;
 };
 
+// Channel tid & 127 on every thread (threads 128-255 repeat 0-127, unused):
+// a load under a divergent branch would be waited for inside the branch.
 template <int T>
 __device__ __forceinline__ void load_output_operands(const Args& A, const Item& it,
                                                      OutputOperands<T>& oo) {
-  const int tid = threadIdx.x;
-  if (tid < kD) {
+  const int c = threadIdx.x & (kD - 1);
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-      oo.gate[t] = A.gate[(it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + tid];
-    oo.nw = bf16_bits_to_f32(A.norm_w[tid]);
-  }
+  for (int t = 0; t < T; ++t)
+    oo.gate[t] = A.gate[(it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + c];
+  oo.nw = bf16_bits_to_f32(A.norm_w[c]);
 }
 
 // ---- prologue: convolution, SiLU, norms, gate projection, decay -------------
@@ -180,19 +180,22 @@ __device__ __forceinline__ void load_output_operands(const Args& A, const Item& 
 // has arrived.
 template <int T>
 struct ConvOperands {
-  uint16_t raw[2][3 + T];  // [part slot][tap0, tap1, tap2, x_0 .. x_{T-1}]
-  float w[2][4];
-  float bias[2];
+  // [part slot][tap0, tap1, tap2, x_0 .. x_{T-1}] as BF16 bits, one per
+  // register: packing two into one would consume each load as it is issued.
+  uint32_t raw[2][3 + T];
+  uint32_t w[2][4];   // BF16 bits of the four taps' weights
+  uint32_t bias[2];   // BF16 bits of the bias (0: none)
 };
 
 template <int T, bool kBias>
 __device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOperands<T>& co) {
   const int tid = threadIdx.x;
   const int c = tid & (kD - 1);
+  const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 7) != 0;  // wave-uniform
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    if (s == 1 && tid >= kD) break;
-    const int part = tid < kD ? s : 2;
+    if (s == 1 && v_wave) break;
+    const int part = v_wave ? 2 : s;
     const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
     const uint16_t* col = A.conv_state + (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
 #pragma unroll
@@ -201,9 +204,9 @@ __device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOpe
     for (int t = 0; t < T; ++t) co.raw[s][3 + t] = A.x[(it.token0 + t) * 3 * it.dim + ch];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      co.w[s][i] = bf16_bits_to_f32(A.conv_w[(static_cast<size_t>(part) * 4 + i) * it.dim +
-                                             static_cast<size_t>(it.h) * kD + c]);
-    co.bias[s] = kBias ? bf16_bits_to_f32(A.conv_b[ch]) : 0.0f;
+      co.w[s][i] = A.conv_w[(static_cast<size_t>(part) * 4 + i) * it.dim +
+                            static_cast<size_t>(it.h) * kD + c];
+    co.bias[s] = kBias ? A.conv_b[ch] : 0u;
   }
 }
 
@@ -214,22 +217,24 @@ __device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& 
                                              const ConvOperands<T>& co) {
   const int tid = threadIdx.x;
   const int c = tid & (kD - 1);
+  const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 7) != 0;  // wave-uniform
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    if (s == 1 && tid >= kD) break;
-    const int part = tid < kD ? s : 2;
+    if (s == 1 && v_wave) break;
+    const int part = v_wave ? 2 : s;
     const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
     uint16_t* col = A.conv_state + (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
-    col[0] = co.raw[s][1];
-    col[1] = co.raw[s][2];
+    col[0] = static_cast<uint16_t>(co.raw[s][1]);
+    col[1] = static_cast<uint16_t>(co.raw[s][2]);
 #pragma unroll
-    for (int t = 0; t < T; ++t) col[2 + t] = co.raw[s][3 + t];
+    for (int t = 0; t < T; ++t) col[2 + t] = static_cast<uint16_t>(co.raw[s][3 + t]);
     float* dst = part == 0 ? &sh.u.in.q[0][0] : part == 1 ? &sh.u.in.k[0][0] : &sh.v[0][0];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float acc = co.bias[s];
+      float acc = bf16_bits_to_f32(co.bias[s]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = fmaf(bf16_bits_to_f32(co.raw[s][t + i]), co.w[s][i], acc);
+      for (int i = 0; i < 4; ++i)
+        acc = fmaf(bf16_bits_to_f32(co.raw[s][t + i]), bf16_bits_to_f32(co.w[s][i]), acc);
       const float y = silu_bf16(acc);
       dst[t * kD + c] = y;
       if constexpr (kRecord) {
@@ -249,9 +254,16 @@ __device__ __forceinline__ void conv_silu(const Args& A, const Item& it, SH& sh)
 }
 
 // Sums of squares of q and k (waves 0 and 1 hold channels 0-63, 64-127) and
-// beta = sigmoid(logit).
+// beta = sigmoid(logit).  The logit of token tid (tid < T) is loaded by
+// load_beta with the other input operands, ahead of the state page.
+template <int T>
+__device__ __forceinline__ float load_beta(const Args& A, const Item& it) {
+  const int t = threadIdx.x < T ? threadIdx.x : T - 1;  // no divergent load
+  return bf16_bits_to_f32(A.beta[(it.token0 + t) * A.H + it.h]);
+}
+
 template <int T, class SH>
-__device__ __forceinline__ void norms_beta(const Args& A, const Item& it, SH& sh) {
+__device__ __forceinline__ void norms_beta(const Item& it, SH& sh, float beta_logit) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (wave < 2) {
 #pragma unroll
@@ -264,8 +276,7 @@ __device__ __forceinline__ void norms_beta(const Args& A, const Item& it, SH& sh
       }
     }
   }
-  if (tid < T)
-    sh.beta[tid] = sigmoid_f32(bf16_bits_to_f32(A.beta[(it.token0 + tid) * A.H + it.h]));
+  if (tid < T) sh.beta[tid] = sigmoid_f32(beta_logit);
 }
 
 // Gate projection raw_g[t][f] = BF16(sum_j F_B[h*128+f][j] f_a[t][j]), exact:
@@ -354,14 +365,68 @@ __device__ __forceinline__ void gate_mfma(const Args& A, const Item& it, SH& sh)
   }
 }
 
+// The same product from operands loaded in one round, so that they can be
+// issued ahead of the state page (record mode, where the page is loaded only
+// after the gate): lane (g, c) of wave w holds F_B rows 32w + 16 tile + c
+// and f_a row c (token c < T) at columns 32q + 8g .. +7, q < 4.  Same
+// accumulation chains and order as gate_mfma.
+struct GateMfmaOperands {
+  uint4 fb[2][4];
+  uint4 fa[4];
+};
+
+template <int T>
+__device__ __forceinline__ void gate_mfma_load(const Args& A, const Item& it,
+                                               GateMfmaOperands& go) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      go.fb[tile][q] = *reinterpret_cast<const uint4*>(
+          A.f_b + (static_cast<size_t>(it.h) * kD + 32 * wave + 16 * tile + c) * kD + 32 * q +
+          8 * g);
+  // Columns c >= T of the product are discarded, and column c of D depends
+  // only on column c of B: those lanes load token T - 1 instead of branching.
+  const int tok = c < T ? c : T - 1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    go.fa[q] = *reinterpret_cast<const uint4*>(A.f_a + (it.token0 + tok) * kD + 32 * q + 8 * g);
+}
+
+template <int T, class SH>
+__device__ __forceinline__ void gate_mfma_compute(const GateMfmaOperands& go, SH& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    const int f0 = 32 * wave + 16 * tile;
+    f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+    for (int q0 = 0; q0 < 4; q0 += 2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+              static_cast<double>(bf16_at(go.fb[tile][q0 + j], e)),
+              static_cast<double>(bf16_at(go.fa[q0 + j], e)), acc[j], 0, 0, 0);
+    if (c < T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sh.u.in.g[c][f0 + g + 4 * r] = static_cast<float>(acc[0][r] + acc[1][r]);
+    }
+  }
+}
+
 // Raw gate to BF16, then the decay of key channel f = tid (threads 0-127);
 // record mode stores raw_g.
 template <int T, bool kRecord, class SH>
-__device__ __forceinline__ void decay(const Args& A, const Item& it, SH& sh) {
+__device__ __forceinline__ void decay(const Args& A, const Item& it, SH& sh, float dt) {
   const int tid = threadIdx.x;
   if (tid < kD) {
     const float e = expf(A.a_log[it.h]);
-    const float dt = A.dt_bias[static_cast<size_t>(it.h) * kD + tid];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float raw_g = round_bf16(sh.u.in.g[t][tid]);
@@ -371,6 +436,11 @@ __device__ __forceinline__ void decay(const Args& A, const Item& it, SH& sh) {
             static_cast<uint16_t>(f32_to_bf16_bits(raw_g));
     }
   }
+}
+
+// dt_bias of key channel tid (threads 0-127), loaded with the input operands.
+__device__ __forceinline__ float load_dt(const Args& A, const Item& it) {
+  return A.dt_bias[static_cast<size_t>(it.h) * kD + (threadIdx.x & (kD - 1))];
 }
 
 template <int T, class SH>

@@ -61,6 +61,13 @@ void kda_step_kernel(const Args A) {
   conv_load<T, kBias>(A, it, co);
   GateOperands go;
   if constexpr (T == 1) gate_load(A, it, go);
+  // Decode has no VGPRs to spare for these two; there they are loaded where
+  // they are used.
+  float beta_logit = 0.0f, dt = 0.0f;
+  if constexpr (T > 1) {
+    beta_logit = load_beta<T>(A, it);
+    dt = load_dt(A, it);
+  }
   OutputOperands<T> oo;
   float4 st[8][2];
   {
@@ -75,10 +82,12 @@ void kda_step_kernel(const Args A) {
 
   // 2. Inputs.
   conv_compute<T, kRecord>(A, it, sh, co);
-  norms_beta<T>(A, it, sh);
+  if constexpr (T == 1) beta_logit = load_beta<T>(A, it);
+  norms_beta<T>(it, sh, beta_logit);
   if constexpr (T == 1) gate_valu(go, sh); else gate_mfma<T>(A, it, sh);
   __syncthreads();
-  decay<T, kRecord>(A, it, sh);
+  if constexpr (T == 1) dt = load_dt(A, it);
+  decay<T, kRecord>(A, it, sh, dt);
   __syncthreads();
 
   // 3. The recurrence, token by token.
@@ -171,8 +180,31 @@ void kda_record_kernel(const Args A) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
 
-  // 1. S0 into the MFMA B-operand layout: [tile][q] = rows 32w + 16 tile + c,
+  // 1. Every input operand in one round (loads of a wave retire in issue
+  //    order, so nothing that the prologue needs may queue behind the page).
+  //    The scheduling barriers keep the three groups in this order.
+  ConvOperands<T> co;
+  conv_load<T, kBias>(A, it, co);
+  __builtin_amdgcn_sched_barrier(0);
+  GateMfmaOperands go;
+  gate_mfma_load<T>(A, it, go);
+  const float beta_logit = load_beta<T>(A, it);
+  const float dt = load_dt(A, it);
+  __builtin_amdgcn_sched_barrier(0);
+  OutputOperands<T> oo;
+  load_output_operands<T>(A, it, oo);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. Convolution, norms, gate projection.
+  conv_compute<T, true>(A, it, sh, co);
+  norms_beta<T>(it, sh, beta_logit);
+  gate_mfma_compute<T>(go, sh);
+  __syncthreads();
+
+  // 3. S0 into the MFMA B-operand layout: [tile][q] = rows 32w + 16 tile + c,
   //    keys 16q + 4g .. +3 (each instruction: 16 rows x 64 contiguous bytes).
+  //    Issued once the gate operands are dead; the decay and the W and X
+  //    tables are computed while it arrives.
   float4 st[2][8];
   {
     const __amdgpu_buffer_rsrc_t page = page_rsrc(A.state, it.rs, it.h, A.H);
@@ -184,16 +216,10 @@ void kda_record_kernel(const Args A) {
   }
   float sink;
   prefetch_page<T>(A, sink);
-
-  // 2. Inputs.
-  conv_silu<T, true, kBias>(A, it, sh);
-  norms_beta<T>(A, it, sh);
-  gate_mfma<T>(A, it, sh);
-  __syncthreads();
-  decay<T, true>(A, it, sh);
+  decay<T, true>(A, it, sh, dt);
   __syncthreads();
 
-  // 3. W and X (thread = key channel), zero rows beyond 2T and T.
+  // 4. W and X (thread = key channel), zero rows beyond 2T and T.
   if (tid < kD) {
     const int key = tid;
     float acc = 1.0f;
@@ -214,10 +240,8 @@ void kda_record_kernel(const Args A) {
     for (int m = T; m < 16; ++m) rt.X[m][key] = 0.0f;
   }
   __syncthreads();  // from here q, k, a and g are dead: P, C and o take their space
-  OutputOperands<T> oo;
-  load_output_operands<T>(A, it, oo);
 
-  // 4. P = S0 W (two 16-row tiles per wave) and, on wave 0, C = W X^T.
+  // 5. P = S0 W (two 16-row tiles per wave) and, on wave 0, C = W X^T.
   //    A operand lane (g, c): W[c][16q + 4g + e]; the K order is shared by
   //    both operands of each product.
   {
@@ -253,7 +277,7 @@ void kda_record_kernel(const Args A) {
   }
   __syncthreads();
 
-  // 5. Per value row v = tid (threads 0-127): the triangular solve for u and o.
+  // 6. Per value row v = tid (threads 0-127): the triangular solve for u and o.
   if (tid < kD) {
     const int v = tid;
     float u[T];
@@ -272,7 +296,7 @@ void kda_record_kernel(const Args A) {
   }
   __syncthreads();
 
-  // 6. Gated RMSNorm.
+  // 7. Gated RMSNorm.
   gated_rmsnorm<T>(A, it, sh, sh.u.out.o, oo);
   keep_alive(A, sink);
 }
