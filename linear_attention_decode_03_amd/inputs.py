@@ -8,6 +8,7 @@ Layouts (row-major, contiguous; "bf16" arrays are uint16 bit patterns):
     x          bf16  [B*T, 3*H*128]   q | k | v channels before the convolution
     conv_w     bf16  [3, 4, H*128]    (part, tap, channel)
     conv_state bf16  [N, 3*H*128, W]  per-slot window of past inputs
+               (f32 when the problem has conv_f32 = 1)
     f_a        bf16  [B*T, 128]       low-rank gate input
     beta       bf16  [B*T, H]         beta logits
     a_log      f32   [H]
@@ -85,7 +86,8 @@ def make_problem(name_or_cfg="tiny_decode", seed=None, **override) -> dict:
     """Builds one seeded problem.  `name_or_cfg` names an entry of CONFIGS or is
     a dict of the same keys; `override` replaces any key (B, H, T, N, W, seed,
     record, gate_mode, padded, fixed_slots, slot_stride, lower_bound, eps,
-    scale)."""
+    scale, conv_f32).  conv_f32 = 1 keeps the convolution pool in FP32 (the
+    same draws, not rounded to BF16)."""
     cfg = dict(CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
     cfg.update(override)
     if seed is not None:
@@ -93,18 +95,20 @@ def make_problem(name_or_cfg="tiny_decode", seed=None, **override) -> dict:
     B, H, T, N, W = (int(cfg[k]) for k in ("B", "H", "T", "N", "W"))
     record = int(cfg.get("record", 0))
     gate_mode = int(cfg.get("gate_mode", 0))
+    conv_f32 = int(cfg.get("conv_f32", 0))
     stride = int(cfg.get("slot_stride", T if T > 1 else 1))
     dim = H * HEAD_DIM
     rng = np.random.default_rng(int(cfg.get("seed", 0)))
 
     p = dict(B=B, H=H, T=T, N=N, W=W, slot_stride=stride, record=record,
-             gate_mode=gate_mode, has_bias=0,
+             gate_mode=gate_mode, has_bias=0, conv_f32=conv_f32,
              lower_bound=float(cfg.get("lower_bound", -5.0)),
              scale=float(cfg.get("scale", 1.0 / math.sqrt(HEAD_DIM))),
              eps=float(cfg.get("eps", 1e-6)))
 
     p["state"] = _normal(rng, (N, H, HEAD_DIM, HEAD_DIM), 0.02)
-    p["conv_state"] = to_bf16(_normal(rng, (N, 3 * dim, W), 1.0))
+    pool = _normal(rng, (N, 3 * dim, W), 1.0)
+    p["conv_state"] = pool if conv_f32 else to_bf16(pool)
     p["conv_w"] = to_bf16(_normal(rng, (3, 4, dim), 0.5))
     p["x"] = to_bf16(_normal(rng, (B * T, 3 * dim), 1.0))
     p["f_a"] = to_bf16(_normal(rng, (B * T, HEAD_DIM), 1.0))

@@ -42,7 +42,7 @@ def build(force: bool = True, src: str = _SRC, lib: str = None) -> str:
 
 class _Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
-                ("B", "H", "N", "W", "T", "slot_stride", "record", "has_bias")] + \
+                ("B", "H", "N", "W", "T", "slot_stride", "record", "has_bias", "conv_f32")] + \
                [(n, ctypes.c_float) for n in ("lower_bound", "scale", "eps")] + \
                [(n, ctypes.c_void_p) for n in
                 ("x", "conv_w", "conv_b", "conv_state", "f_a", "beta", "a_log", "dt_bias",
@@ -94,8 +94,9 @@ def _ptr(p, key):
     a = p.get(key)
     if a is None:
         return None
-    if a.dtype != _LAYOUT[key] or not a.flags["C_CONTIGUOUS"]:
-        raise TypeError(f"oracle operand {key}: need contiguous {_LAYOUT[key].__name__}")
+    want = np.float32 if key == "conv_state" and p.get("conv_f32") else _LAYOUT[key]
+    if a.dtype != want or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"oracle operand {key}: need contiguous {want.__name__}")
     return a.ctypes.data
 
 
@@ -108,6 +109,7 @@ def run(p: dict, items=None, taps: bool = False):
     lib = _load()
     prob = _Problem(**{n: int(p[n]) for n in
                        ("B", "H", "N", "W", "T", "slot_stride", "record", "has_bias")},
+                    conv_f32=int(p.get("conv_f32", 0)),
                     lower_bound=float(p["lower_bound"]), scale=float(p["scale"]),
                     eps=float(p["eps"]),
                     **{k: _ptr(p, k) for k in _LAYOUT})

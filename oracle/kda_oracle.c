@@ -111,12 +111,13 @@ void kda_oracle_gated_rmsnorm(const float* o_bf, const uint16_t* gate,
 typedef struct kda_oracle_problem {
   /* sizes and switches */
   int B, H, N, W, T, slot_stride, record, has_bias;
+  int conv_f32;             /* 1: the convolution pool holds FP32, else BF16 */
   float lower_bound, scale, eps;
   /* operands: host memory, the same layouts as the device library */
   const uint16_t* x;        /* [B*T, 3*H*128] q|k|v before the convolution */
   const uint16_t* conv_w;   /* [3, 4, H*128] */
   const uint16_t* conv_b;   /* [3*H*128], read iff has_bias */
-  uint16_t* conv_state;     /* [N, 3*H*128, W], updated in place */
+  void* conv_state;         /* [N, 3*H*128, W] BF16 or FP32 (conv_f32), in place */
   const uint16_t* f_a;      /* [B*T, 128] gate low-rank input */
   const uint16_t* beta;     /* [B*T, H] logits */
   const float* a_log;       /* [H] */
@@ -195,18 +196,26 @@ static void run_item(const kda_oracle_problem* P, int b, int h,
   /* Short causal convolution over the window
    * [tap0, tap1, tap2, x_0, ..., x_{T-1}] and SiLU, BF16-rounded. */
   float Y[3][MAX_T][D]; /* q, k, v */
-  uint16_t window[3][D][3 + MAX_T];
+  /* The window holds values of the pool's element type (kernel body: the
+   * taps are read in that type and the inputs are converted to it); the
+   * arithmetic reads them as FP32, which both types convert to exactly. */
+  float window[3][D][3 + MAX_T];
   for (int p = 0; p < 3; ++p) {
     for (int c = 0; c < D; ++c) {
       size_t ch = (size_t)p * dim + (size_t)h * D + c;
-      const uint16_t* col = P->conv_state + ((size_t)cs * 3 * dim + ch) * W;
-      for (int i = 0; i < 3; ++i) window[p][c][i] = col[off + i];
-      for (int t = 0; t < T; ++t) window[p][c][3 + t] = P->x[(token0 + t) * 3 * dim + ch];
+      size_t base = ((size_t)cs * 3 * dim + ch) * W;
+      for (int i = 0; i < 3; ++i) {
+        size_t at = base + off + i;
+        if (P->conv_f32) window[p][c][i] = ((const float*)P->conv_state)[at];
+        else window[p][c][i] = bf16_to_float(((const uint16_t*)P->conv_state)[at]);
+      }
+      for (int t = 0; t < T; ++t)
+        window[p][c][3 + t] = bf16_to_float(P->x[(token0 + t) * 3 * dim + ch]);
       for (int t = 0; t < T; ++t) {
         float acc = P->has_bias ? bf16_to_float(P->conv_b[ch]) : 0.0f;
         for (int i = 0; i < TAPS; ++i) {
           float w = bf16_to_float(P->conv_w[((size_t)p * TAPS + i) * dim + (size_t)h * D + c]);
-          acc = fmaf(bf16_to_float(window[p][c][t + i]), w, acc);
+          acc = fmaf(window[p][c][t + i], w, acc);
         }
         Y[p][t][c] = kda_oracle_silu_bf16(acc);
       }
@@ -288,14 +297,18 @@ static void run_item(const kda_oracle_problem* P, int b, int h,
     }
   }
 
-  /* Convolution window [tap1, tap2, x_0, ..., x_{T-1}], bits copied. */
+  /* Convolution window [tap1, tap2, x_0, ..., x_{T-1}] in the pool's type:
+   * every value came from that type or from BF16, so the conversion back is
+   * exact and the bits are those read. */
   for (int p = 0; p < 3; ++p) {
     for (int c = 0; c < D; ++c) {
       size_t ch = (size_t)p * dim + (size_t)h * D + c;
-      uint16_t* col = P->conv_state + ((size_t)cs * 3 * dim + ch) * W;
-      col[0] = window[p][c][1];
-      col[1] = window[p][c][2];
-      for (int t = 0; t < T; ++t) col[2 + t] = window[p][c][3 + t];
+      size_t base = ((size_t)cs * 3 * dim + ch) * W;
+      for (int j = 0; j < 2 + T; ++j) {
+        float v = window[p][c][1 + j];
+        if (P->conv_f32) ((float*)P->conv_state)[base + j] = v;
+        else ((uint16_t*)P->conv_state)[base + j] = float_to_bf16(v);
+      }
     }
   }
 

@@ -22,7 +22,13 @@ MUTANTS = [
     ("conv tap order reversed", "window[p][c][t + i]", "window[p][c][t + 3 - i]"),
     ("conv weight of wrong head",
      "((size_t)p * TAPS + i) * dim + (size_t)h * D + c]", "((size_t)p * TAPS + i) * dim + c]"),
-    ("conv window starts at column 0", "window[p][c][i] = col[off + i]", "window[p][c][i] = col[i]"),
+    ("conv window starts at column 0", "size_t at = base + off + i;", "size_t at = base + i;"),
+    ("FP32 conv taps rounded to BF16 on read",
+     "if (P->conv_f32) window[p][c][i] = ((const float*)P->conv_state)[at];",
+     "if (P->conv_f32) window[p][c][i] = round_bf16(((const float*)P->conv_state)[at]);"),
+    ("FP32 conv window written rounded to BF16",
+     "if (P->conv_f32) ((float*)P->conv_state)[base + j] = v;",
+     "if (P->conv_f32) ((float*)P->conv_state)[base + j] = round_bf16(v);"),
     ("silu sign", "float e = (float)exp(-(double)x);", "float e = (float)exp((double)x);"),
     ("silu not rounded to bf16", "  return round_bf16(y);\n}", "  return y;\n}"),
     ("k not normalised", "k_hat[t][c] = Y[1][t][c] * fk;", "k_hat[t][c] = Y[1][t][c];"),
@@ -56,7 +62,7 @@ MUTANTS = [
      "*read_slot = P->slots[(size_t)b * P->slot_stride];"),
     ("verify writes every token to the read slot",
      "int target = T == 1 ? rs : P->slots[(size_t)b * P->slot_stride + t];", "int target = rs;"),
-    ("window shift off by one", "col[0] = window[p][c][1];", "col[0] = window[p][c][0];"),
+    ("window shift off by one", "float v = window[p][c][1 + j];", "float v = window[p][c][j];"),
     ("record k after the norm", "kg[c] = float_to_bf16(Y[1][t][c]);", "kg[c] = float_to_bf16(k_hat[t][c]);"),
     ("padding writes no zeros",
      "for (int c = 0; c < D; ++c) P->out[(token0 + t) * dim + (size_t)h * D + c] = 0;", ";"),

@@ -8,6 +8,7 @@ formulation.  Which step each pin covers:
 
   slot resolution, padding ............ test_padding_*, test_contract_errors
   convolution (tap order, window) ..... test_conv_tap_selection, test_conv_window_update
+  FP32 convolution pool ............... the same two with conv_f32, test_conv_f32_reduces_to_bf16
   SiLU stage .......................... test_silu_textbook
   L2 norm, q/k roles, o = S^T q ....... test_zero_state_closed_form, test_delta_rule_*
   gate projection (indexing) .......... test_gate_one_hot
@@ -277,11 +278,19 @@ def test_silu_textbook(oracle_lib):
         assert got == float(w) or (math.isnan(got) and math.isnan(w)), x
 
 
-@pytest.mark.parametrize("T", [1, 3])
-def test_conv_tap_selection(oracle_lib, T):
+def pool_values(p, cs, ch, col):
+    """FP32 values of convolution-pool entries (BF16 bits or FP32)."""
+    v = p["conv_state"][cs][ch, col]
+    return v.astype(np.float32) if p.get("conv_f32") else from_bf16(v)
+
+
+@pytest.mark.parametrize("T,conv_f32", [(1, 0), (3, 0), (1, 1), (3, 1)])
+def test_conv_tap_selection(oracle_lib, T, conv_f32):
     """One-hot tap weights select one window entry: weight i selects
-    window[t + i] of [conv[off], conv[off+1], conv[off+2], x_0, ..., x_{T-1}]."""
-    p = small(T=T, B=2, H=2)
+    window[t + i] of [conv[off], conv[off+1], conv[off+2], x_0, ..., x_{T-1}].
+    With an FP32 pool the taps enter the SiLU unrounded (the pool draws are
+    not BF16 values)."""
+    p = small(T=T, B=2, H=2, conv_f32=conv_f32)
     if T > 1:
         p["accepted"][:] = [2, 3]
     dim = p["H"] * D
@@ -298,17 +307,20 @@ def test_conv_tap_selection(oracle_lib, T):
             for h in range(p["H"]):
                 for part, name in enumerate(("q", "k", "v")):
                     ch = part * dim + h * D + np.arange(D)
-                    window = [from_bf16(p["conv_state"][cs][ch, off + i]) for i in range(3)]
+                    window = [pool_values(p, cs, ch, off + i) for i in range(3)]
                     window += [from_bf16(p["x"][b * T + t, ch]) for t in range(T)]
                     for t in range(T):
                         want = bf16_of_f64(silu64(window[t + tap]))
                         assert np.array_equal(taps[name][b, h, t], want)
 
 
-def test_conv_window_update(oracle_lib):
-    """Window after the step: [tap1, tap2, x_0, ..., x_{T-1}], bits copied."""
+@pytest.mark.parametrize("conv_f32", [0, 1])
+def test_conv_window_update(oracle_lib, conv_f32):
+    """Window after the step: [tap1, tap2, x_0, ..., x_{T-1}] in the pool's
+    type: taps keep their bits, the BF16 inputs are stored exactly (as BF16
+    bits, or as their FP32 values in an FP32 pool)."""
     for T in (1, 3):
-        p = small(T=T, B=2, H=1)
+        p = small(T=T, B=2, H=1, conv_f32=conv_f32)
         if T > 1:
             p["accepted"][:] = [3, 2]
         before = inputs.copy_problem(p)
@@ -322,8 +334,24 @@ def test_conv_window_update(oracle_lib):
             assert np.array_equal(new[:, 0], old[:, off + 1])
             assert np.array_equal(new[:, 1], old[:, off + 2])
             for t in range(T):
-                assert np.array_equal(new[:, 2 + t], before["x"][b * T + t, :3 * dim])
+                x = before["x"][b * T + t, :3 * dim]
+                assert np.array_equal(new[:, 2 + t], from_bf16(x) if conv_f32 else x)
             assert np.array_equal(new[:, 2 + T:], old[:, 2 + T:])
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_conv_f32_reduces_to_bf16(oracle_lib, T):
+    """An FP32 pool holding BF16 values (exactly) gives the BF16 pool's step
+    bit for bit, and its window afterwards holds the BF16 window's values."""
+    p = small(T=T, B=3, H=2)
+    q = inputs.copy_problem(p)
+    q["conv_f32"] = 1
+    q["conv_state"] = from_bf16(p["conv_state"]).reshape(p["conv_state"].shape).copy()
+    oracle_lib.run(p)
+    oracle_lib.run(q)
+    assert np.array_equal(q["out"], p["out"])
+    assert np.array_equal(q["state"].view(np.uint32), p["state"].view(np.uint32))
+    assert np.array_equal(q["conv_state"], from_bf16(p["conv_state"]).reshape(p["conv_state"].shape))
 
 
 def test_gate_one_hot(oracle_lib):
