@@ -55,7 +55,8 @@ def algorithmic_bytes(p) -> int:
     """Bytes the method must move for one launch (each operand once):
     per live item: the 64 KiB state page read, 64 KiB written per stored
     token (1 for decode, T for verify, 0 for record), records T KiB, the
-    3 read taps and T+2 written columns of its 384 convolution channels,
+    3 read taps and T+2 written columns of its 384 convolution channels
+    (2 bytes each, 4 with an FP32 pool),
     x (768 B), gate (256 B), beta (2 B) and out (256 B) per token; per padded
     item its 256 B of zeros per token; per live request f_a (256 B per
     token); the slot tables; once per launch the weights (F_B, conv weights,
@@ -69,8 +70,9 @@ def algorithmic_bytes(p) -> int:
     live_req = live // H
     pad = B * H - live
     stored = 0 if p["record"] else (1 if T == 1 else T)
+    ce = 4 if p.get("conv_f32") else 2  # bytes per convolution-pool entry
     per_live = (65536 * (1 + stored) + (1024 * T if p["record"] else 0)
-                + 3 * D * 3 * 2 + 3 * D * (T + 2) * 2 + T * (768 + 256 + 2 + 256))
+                + 3 * D * 3 * ce + 3 * D * (T + 2) * ce + T * (768 + 256 + 2 + 256))
     total = live * per_live + pad * 256 * T + live_req * 256 * T
     total += int(np.asarray(p["slots"]).nbytes) + (B * 4 if T > 1 else 0)
     total += H * (3 * 4 * D * 2 + D * D * 2 + D * 4 + 4) + D * 2
@@ -163,6 +165,8 @@ def main():
     ap.add_argument("--ahead", type=int, default=-1)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cold-launches", type=int, default=20)
+    ap.add_argument("--conv-f32", action="store_true",
+                    help="keep the convolution pool in FP32 (kda_*_f32conv)")
     ap.add_argument("--mode", choices=["kda", "copy"], default="kda")
     args = ap.parse_args()
 
@@ -184,7 +188,7 @@ def main():
     if replay:
         p = inputs.make_replay_problem(args.workload)
     else:
-        p = inputs.make_problem(args.workload)
+        p = inputs.make_problem(args.workload, conv_f32=int(args.conv_f32))
     print(f"[bench] workload {args.workload}: inputs ready", file=sys.stderr, flush=True)
     d = _gpu.to_device(p)
 
@@ -238,7 +242,8 @@ def main():
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
     if not replay:
-        extra = {"record": p["record"], "gate_mode": p["gate_mode"]}
+        extra = {"record": p["record"], "gate_mode": p["gate_mode"],
+                 "conv_pool": "f32" if p["conv_f32"] else "bf16"}
     else:
         extra = {"tokens_applied": int(p["n"].sum())}
     result = {

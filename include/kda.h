@@ -135,6 +135,34 @@ kda_status kda_verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t*
                       int record, int gate_mode, int ahead, void* stream);
 
 /*
+ * kda_decode_f32conv, kda_verify_f32conv -- kda_decode and kda_verify for a
+ * convolution pool held in FP32 (the kernel body reads the window taps in
+ * the pool's element type and writes the window back in it).  Arguments as
+ * for kda_decode / kda_verify except
+ *   conv_state  [N, 3*H*128, W] FP32: taps enter the convolution unrounded;
+ *               the window is rewritten [tap1, tap2, x_0, ..] with each BF16
+ *               input stored as its exact FP32 value.
+ * Everything else (layouts, ownership, errors, caller contract) is the same.
+ */
+kda_status kda_decode_f32conv(const uint16_t* x, const uint16_t* conv_w,
+                              const uint16_t* conv_b, float* conv_state, const uint16_t* f_a,
+                              const uint16_t* beta, const float* a_log, const float* dt_bias,
+                              const int32_t* slots, float* state, uint16_t* out,
+                              const uint16_t* gate, const uint16_t* norm_w, float lower_bound,
+                              float scale, float eps, const uint16_t* f_b, int B, int H, int N,
+                              int W, int gate_mode, int ahead, void* stream);
+
+kda_status kda_verify_f32conv(const uint16_t* x, const uint16_t* conv_w,
+                              const uint16_t* conv_b, float* conv_state, const uint16_t* f_a,
+                              const uint16_t* beta, const float* a_log, const float* dt_bias,
+                              const int32_t* slots, float* state, uint16_t* out,
+                              const uint16_t* gate, const uint16_t* norm_w, float lower_bound,
+                              float scale, float eps, const uint16_t* f_b,
+                              const int32_t* accepted, float* rec_u, uint16_t* rec_kg, int B,
+                              int H, int N, int W, int T, int slot_stride, int record,
+                              int gate_mode, int ahead, void* stream);
+
+/*
  * kda_replay -- RecoverSSM: the state after the first n accepted tokens of a
  * record-mode kda_verify, rebuilt from the checkpoint page that verify read
  * and the records it wrote (the KdaWide class docstring's RecoverSSM mode;

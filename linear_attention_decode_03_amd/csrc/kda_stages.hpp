@@ -16,7 +16,7 @@ struct Args {
   const uint16_t* x;
   const uint16_t* conv_w;
   const uint16_t* conv_b;
-  uint16_t* conv_state;
+  void* conv_state;  // BF16 bits, or FP32 when conv_f32
   const uint16_t* f_a;
   const uint16_t* beta;
   const float* a_log;
@@ -33,6 +33,7 @@ struct Args {
   float lower_bound, scale, eps;
   int B, H, N, W, slot_stride;
   int ahead;  // prefetch distance in items (0: off), a multiple of 8
+  int conv_f32;  // the convolution pool holds FP32 values
 };
 
 // ---- shared memory -----------------------------------------------------------
@@ -180,14 +181,20 @@ __device__ __forceinline__ void load_output_operands(const Args& A, const Item& 
 // has arrived.
 template <int T>
 struct ConvOperands {
-  // [part slot][tap0, tap1, tap2, x_0 .. x_{T-1}] as BF16 bits, one per
-  // register: packing two into one would consume each load as it is issued.
+  // [part slot][tap0, tap1, tap2, x_0 .. x_{T-1}]: taps in the pool's type
+  // (BF16 or FP32 bits), inputs as BF16 bits, one per register: packing two
+  // into one would consume each load as it is issued.
   uint32_t raw[2][3 + T];
   uint32_t w[2][4];   // BF16 bits of the four taps' weights
   uint32_t bias[2];   // BF16 bits of the bias (0: none)
 };
 
-template <int T, bool kBias>
+template <bool kConvF32>
+__device__ __forceinline__ float tap_value(uint32_t bits) {
+  return kConvF32 ? __uint_as_float(bits) : bf16_bits_to_f32(bits);
+}
+
+template <int T, bool kBias, bool kConvF32>
 __device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOperands<T>& co) {
   const int tid = threadIdx.x;
   const int c = tid & (kD - 1);
@@ -197,9 +204,11 @@ __device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOpe
     if (s == 1 && v_wave) break;
     const int part = v_wave ? 2 : s;
     const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
-    const uint16_t* col = A.conv_state + (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
+    const size_t base = (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W + it.off;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) co.raw[s][i] = col[it.off + i];
+    for (int i = 0; i < 3; ++i)
+      co.raw[s][i] = kConvF32 ? static_cast<const uint32_t*>(A.conv_state)[base + i]
+                              : static_cast<const uint16_t*>(A.conv_state)[base + i];
 #pragma unroll
     for (int t = 0; t < T; ++t) co.raw[s][3 + t] = A.x[(it.token0 + t) * 3 * it.dim + ch];
 #pragma unroll
@@ -210,9 +219,10 @@ __device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOpe
   }
 }
 
-// The window is rewritten in place after it was read: [tap1, tap2, x_0 ..];
+// The window is rewritten in place after it was read: [tap1, tap2, x_0 ..]
+// in the pool's type (an FP32 pool receives the inputs' exact FP32 values);
 // record mode stores k.
-template <int T, bool kRecord, class SH>
+template <int T, bool kRecord, bool kConvF32, class SH>
 __device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& sh,
                                              const ConvOperands<T>& co) {
   const int tid = threadIdx.x;
@@ -223,18 +233,30 @@ __device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& 
     if (s == 1 && v_wave) break;
     const int part = v_wave ? 2 : s;
     const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
-    uint16_t* col = A.conv_state + (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
-    col[0] = static_cast<uint16_t>(co.raw[s][1]);
-    col[1] = static_cast<uint16_t>(co.raw[s][2]);
+    const size_t base = (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
+    if constexpr (kConvF32) {
+      uint32_t* col = static_cast<uint32_t*>(A.conv_state) + base;
+      col[0] = co.raw[s][1];
+      col[1] = co.raw[s][2];
 #pragma unroll
-    for (int t = 0; t < T; ++t) col[2 + t] = static_cast<uint16_t>(co.raw[s][3 + t]);
+      for (int t = 0; t < T; ++t) col[2 + t] = co.raw[s][3 + t] << 16;
+    } else {
+      uint16_t* col = static_cast<uint16_t*>(A.conv_state) + base;
+      col[0] = static_cast<uint16_t>(co.raw[s][1]);
+      col[1] = static_cast<uint16_t>(co.raw[s][2]);
+#pragma unroll
+      for (int t = 0; t < T; ++t) col[2 + t] = static_cast<uint16_t>(co.raw[s][3 + t]);
+    }
     float* dst = part == 0 ? &sh.u.in.q[0][0] : part == 1 ? &sh.u.in.k[0][0] : &sh.v[0][0];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float acc = bf16_bits_to_f32(co.bias[s]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc = fmaf(bf16_bits_to_f32(co.raw[s][t + i]), bf16_bits_to_f32(co.w[s][i]), acc);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t r = co.raw[s][t + i];
+        const float term = t + i < 3 ? tap_value<kConvF32>(r) : bf16_bits_to_f32(r);
+        acc = fmaf(term, bf16_bits_to_f32(co.w[s][i]), acc);
+      }
       const float y = silu_bf16(acc);
       dst[t * kD + c] = y;
       if constexpr (kRecord) {
@@ -244,13 +266,6 @@ __device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& 
       }
     }
   }
-}
-
-template <int T, bool kRecord, bool kBias, class SH>
-__device__ __forceinline__ void conv_silu(const Args& A, const Item& it, SH& sh) {
-  ConvOperands<T> co;
-  conv_load<T, kBias>(A, it, co);
-  conv_compute<T, kRecord>(A, it, sh, co);
 }
 
 // Sums of squares of q and k (waves 0 and 1 hold channels 0-63, 64-127) and

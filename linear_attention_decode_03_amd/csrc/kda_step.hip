@@ -41,7 +41,7 @@ namespace {
 // 16-byte access of a wave covers four 256-byte row segments 16 KiB apart,
 // which spreads each instruction over more HBM channels; a row's keys sit in
 // one 16-lane DPP row.
-template <int T, bool kRecord, bool kBias>
+template <int T, bool kRecord, bool kBias, bool kConvF32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void kda_step_kernel(const Args A) {
   Item it;
@@ -58,7 +58,7 @@ void kda_step_kernel(const Args A) {
   // 1. Input operands first, then the state page (one buffer resource per
   //    64 KiB page): the inputs are used while the page is still arriving.
   ConvOperands<T> co;
-  conv_load<T, kBias>(A, it, co);
+  conv_load<T, kBias, kConvF32>(A, it, co);
   GateOperands go;
   if constexpr (T == 1) gate_load(A, it, go);
   // Decode has no VGPRs to spare for these two; there they are loaded where
@@ -81,7 +81,7 @@ void kda_step_kernel(const Args A) {
   prefetch_page<T>(A, sink);
 
   // 2. Inputs.
-  conv_compute<T, kRecord>(A, it, sh, co);
+  conv_compute<T, kRecord, kConvF32>(A, it, sh, co);
   if constexpr (T == 1) beta_logit = load_beta<T>(A, it);
   norms_beta<T>(it, sh, beta_logit);
   if constexpr (T == 1) gate_valu(go, sh); else gate_mfma<T>(A, it, sh);
@@ -167,7 +167,7 @@ void kda_step_kernel(const Args A) {
 // layout (lane (g, c) of wave w holds rows 32w + 16 tile + c, keys
 // 16q + 4g + [0, 4)).  Used when |lower_bound| <= 10, so that every A_t and
 // 1 / A_t stays a normal FP32 number (|log A_t| <= 80).
-template <int T, bool kBias>
+template <int T, bool kBias, bool kConvF32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void kda_record_kernel(const Args A) {
   Item it;
@@ -184,7 +184,7 @@ void kda_record_kernel(const Args A) {
   //    order, so nothing that the prologue needs may queue behind the page).
   //    The scheduling barriers keep the three groups in this order.
   ConvOperands<T> co;
-  conv_load<T, kBias>(A, it, co);
+  conv_load<T, kBias, kConvF32>(A, it, co);
   __builtin_amdgcn_sched_barrier(0);
   GateMfmaOperands go;
   gate_mfma_load<T>(A, it, go);
@@ -196,7 +196,7 @@ void kda_record_kernel(const Args A) {
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. Convolution, norms, gate projection.
-  conv_compute<T, true>(A, it, sh, co);
+  conv_compute<T, true, kConvF32>(A, it, sh, co);
   norms_beta<T>(it, sh, beta_logit);
   gate_mfma_compute<T>(go, sh);
   __syncthreads();
@@ -327,25 +327,28 @@ kda_status check(const Args& A, int T, int record, int gate_mode) {
 // stay normal FP32 numbers (|lower_bound| <= 10, at most 8 tokens: |log A_t| <= 80).
 constexpr float kRecordBound = 10.0f;
 
-template <int T, bool kRecord>
-kda_status launch_t(const Args& A, hipStream_t stream) {
+template <int T, bool kRecord, bool kBias, bool kConvF32>
+kda_status launch_v(const Args& A, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(A.B * A.H));
   const dim3 block(kThreads);
-  const bool bias = A.conv_b != nullptr;
   if constexpr (kRecord && T > 1) {
     if (fabsf(A.lower_bound) <= kRecordBound) {
-      if (bias)
-        hipLaunchKernelGGL((kda_record_kernel<T, true>), grid, block, 0, stream, A);
-      else
-        hipLaunchKernelGGL((kda_record_kernel<T, false>), grid, block, 0, stream, A);
+      hipLaunchKernelGGL((kda_record_kernel<T, kBias, kConvF32>), grid, block, 0, stream, A);
       return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
     }
   }
-  if (bias)
-    hipLaunchKernelGGL((kda_step_kernel<T, kRecord, true>), grid, block, 0, stream, A);
-  else
-    hipLaunchKernelGGL((kda_step_kernel<T, kRecord, false>), grid, block, 0, stream, A);
+  hipLaunchKernelGGL((kda_step_kernel<T, kRecord, kBias, kConvF32>), grid, block, 0, stream, A);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <int T, bool kRecord>
+kda_status launch_t(const Args& A, hipStream_t stream) {
+  const bool bias = A.conv_b != nullptr;
+  if (A.conv_f32)
+    return bias ? launch_v<T, kRecord, true, true>(A, stream)
+                : launch_v<T, kRecord, false, true>(A, stream);
+  return bias ? launch_v<T, kRecord, true, false>(A, stream)
+              : launch_v<T, kRecord, false, false>(A, stream);
 }
 
 template <bool kRecord>
@@ -375,11 +378,12 @@ int resolve_ahead(int ahead) {
 }
 
 Args pack(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
-          uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta, const float* a_log,
+          void* conv_state, const uint16_t* f_a, const uint16_t* beta, const float* a_log,
           const float* dt_bias, const int32_t* slots, float* state, uint16_t* out,
           const uint16_t* gate, const uint16_t* norm_w, float lower_bound, float scale,
           float eps, const uint16_t* f_b, const int32_t* accepted, float* rec_u,
-          uint16_t* rec_kg, int B, int H, int N, int W, int slot_stride, int ahead) {
+          uint16_t* rec_kg, int B, int H, int N, int W, int slot_stride, int ahead,
+          int conv_f32 = 0) {
   Args A;
   A.x = x; A.conv_w = conv_w; A.conv_b = conv_b; A.conv_state = conv_state; A.f_a = f_a;
   A.beta = beta; A.a_log = a_log; A.dt_bias = dt_bias; A.slots = slots; A.state = state;
@@ -388,7 +392,42 @@ Args pack(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
   A.lower_bound = lower_bound; A.scale = scale; A.eps = eps;
   A.B = B; A.H = H; A.N = N; A.W = W; A.slot_stride = slot_stride;
   A.ahead = resolve_ahead(ahead);
+  A.conv_f32 = conv_f32;
   return A;
+}
+
+
+
+kda_status decode(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                  void* conv_state, int conv_f32, const uint16_t* f_a, const uint16_t* beta,
+                  const float* a_log, const float* dt_bias, const int32_t* slots, float* state,
+                  uint16_t* out, const uint16_t* gate, const uint16_t* norm_w,
+                  float lower_bound, float scale, float eps, const uint16_t* f_b, int B, int H,
+                  int N, int W, int gate_mode, int ahead, void* stream) {
+  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                      out, gate, norm_w, lower_bound, scale, eps, f_b, nullptr, nullptr,
+                      nullptr, B, H, N, W, 1, ahead, conv_f32);
+  const kda_status s = check(A, 1, 0, gate_mode);
+  if (s != KDA_OK || B == 0) return s;
+  return launch<false>(A, 1, static_cast<hipStream_t>(stream));
+}
+
+kda_status verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                  void* conv_state, int conv_f32, const uint16_t* f_a, const uint16_t* beta,
+                  const float* a_log, const float* dt_bias, const int32_t* slots, float* state,
+                  uint16_t* out, const uint16_t* gate, const uint16_t* norm_w,
+                  float lower_bound, float scale, float eps, const uint16_t* f_b,
+                  const int32_t* accepted, float* rec_u, uint16_t* rec_kg, int B, int H, int N,
+                  int W, int T, int slot_stride, int record, int gate_mode, int ahead,
+                  void* stream) {
+  if (T == 1) return KDA_ERR_TOKENS;  // a one-token step is kda_decode
+  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                      out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg,
+                      B, H, N, W, slot_stride, ahead, conv_f32);
+  const kda_status s = check(A, T, record, gate_mode);
+  if (s != KDA_OK || B == 0) return s;
+  return record ? launch<true>(A, T, static_cast<hipStream_t>(stream))
+                : launch<false>(A, T, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -416,12 +455,21 @@ kda_status kda_decode(const uint16_t* x, const uint16_t* conv_w, const uint16_t*
                       const uint16_t* norm_w, float lower_bound, float scale, float eps,
                       const uint16_t* f_b, int B, int H, int N, int W, int gate_mode, int ahead,
                       void* stream) {
-  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
-                      out, gate, norm_w, lower_bound, scale, eps, f_b, nullptr, nullptr,
-                      nullptr, B, H, N, W, 1, ahead);
-  const kda_status s = check(A, 1, 0, gate_mode);
-  if (s != KDA_OK || B == 0) return s;
-  return launch<false>(A, 1, static_cast<hipStream_t>(stream));
+  return decode(x, conv_w, conv_b, conv_state, 0, f_a, beta, a_log, dt_bias, slots, state, out,
+                gate, norm_w, lower_bound, scale, eps, f_b, B, H, N, W, gate_mode, ahead,
+                stream);
+}
+
+kda_status kda_decode_f32conv(const uint16_t* x, const uint16_t* conv_w,
+                              const uint16_t* conv_b, float* conv_state, const uint16_t* f_a,
+                              const uint16_t* beta, const float* a_log, const float* dt_bias,
+                              const int32_t* slots, float* state, uint16_t* out,
+                              const uint16_t* gate, const uint16_t* norm_w, float lower_bound,
+                              float scale, float eps, const uint16_t* f_b, int B, int H, int N,
+                              int W, int gate_mode, int ahead, void* stream) {
+  return decode(x, conv_w, conv_b, conv_state, 1, f_a, beta, a_log, dt_bias, slots, state, out,
+                gate, norm_w, lower_bound, scale, eps, f_b, B, H, N, W, gate_mode, ahead,
+                stream);
 }
 
 kda_status kda_verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
@@ -432,16 +480,24 @@ kda_status kda_verify(const uint16_t* x, const uint16_t* conv_w, const uint16_t*
                       const uint16_t* f_b, const int32_t* accepted, float* rec_u,
                       uint16_t* rec_kg, int B, int H, int N, int W, int T, int slot_stride,
                       int record, int gate_mode, int ahead, void* stream) {
-  if (T == 1) return KDA_ERR_TOKENS;  // a one-token step is kda_decode
-  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
-                      out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg,
-                      B, H, N, W, slot_stride, ahead);
-  const kda_status s = check(A, T, record, gate_mode);
-  if (s != KDA_OK || B == 0) return s;
-  return record ? launch<true>(A, T, static_cast<hipStream_t>(stream))
-                : launch<false>(A, T, static_cast<hipStream_t>(stream));
+  return verify(x, conv_w, conv_b, conv_state, 0, f_a, beta, a_log, dt_bias, slots, state, out,
+                gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg, B, H, N,
+                W, T, slot_stride, record, gate_mode, ahead, stream);
 }
 
+kda_status kda_verify_f32conv(const uint16_t* x, const uint16_t* conv_w,
+                              const uint16_t* conv_b, float* conv_state, const uint16_t* f_a,
+                              const uint16_t* beta, const float* a_log, const float* dt_bias,
+                              const int32_t* slots, float* state, uint16_t* out,
+                              const uint16_t* gate, const uint16_t* norm_w, float lower_bound,
+                              float scale, float eps, const uint16_t* f_b,
+                              const int32_t* accepted, float* rec_u, uint16_t* rec_kg, int B,
+                              int H, int N, int W, int T, int slot_stride, int record,
+                              int gate_mode, int ahead, void* stream) {
+  return verify(x, conv_w, conv_b, conv_state, 1, f_a, beta, a_log, dt_bias, slots, state, out,
+                gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u, rec_kg, B, H, N,
+                W, T, slot_stride, record, gate_mode, ahead, stream);
+}
 
 const char* kda_status_string(kda_status status) {
   switch (status) {

@@ -41,6 +41,10 @@ def load_library(path: str = LIB_PATH):
         lib.kda_decode.argtypes = _OPERANDS + [_I] * 6 + [_P]
         lib.kda_verify.restype = _I
         lib.kda_verify.argtypes = _OPERANDS + [_P] * 3 + [_I] * 9 + [_P]
+        lib.kda_decode_f32conv.restype = _I
+        lib.kda_decode_f32conv.argtypes = lib.kda_decode.argtypes
+        lib.kda_verify_f32conv.restype = _I
+        lib.kda_verify_f32conv.argtypes = lib.kda_verify.argtypes
         lib.kda_validate.restype = _I
         lib.kda_validate.argtypes = _OPERANDS + [_P] * 3 + [_I] * 8
         lib.kda_replay.restype = _I
@@ -100,7 +104,8 @@ def _check_common(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slot
     dev = state.device
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     for name, t, dt, nd in (("x", x, bf, 2), ("conv_w", conv_w, bf, 3), ("conv_b", conv_b, bf, 1),
-                            ("conv_state", conv_state, bf, 3), ("f_a", f_a, bf, 2),
+                            ("conv_state", conv_state, conv_state.dtype if conv_state.dtype in
+                             (bf, f32) else bf, 3), ("f_a", f_a, bf, 2),
                             ("beta", beta, bf, 2), ("a_log", a_log, f32, 1),
                             ("dt_bias", dt_bias, f32, 1), ("state", state, f32, 4),
                             ("out", out, bf, 2), ("gate", gate, bf, 2), ("norm_w", norm_w, bf, 1),
@@ -131,12 +136,17 @@ def _stream(stream):
 
 def kda_decode(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
                gate, norm_w, lower_bound, scale, eps, f_b, gate_mode=0, ahead=-1, stream=None):
-    """One decode step (T = 1); see kda_decode in include/kda.h.  Enqueued on
-    `stream` (default: torch's current stream); returns without waiting."""
+    """One decode step (T = 1); see kda_decode in include/kda.h (an FP32
+    conv_state runs kda_decode_f32conv).  Enqueued on `stream` (default:
+    torch's current stream); returns without waiting."""
+    import torch
+
     B, H, N, W = _sizes(x, state, conv_state, 1)
     _check_common(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
                   gate, norm_w, f_b, B, H, 1)
-    status = load_library().kda_decode(
+    lib = load_library()
+    entry = lib.kda_decode_f32conv if conv_state.dtype == torch.float32 else lib.kda_decode
+    status = entry(
         _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
         _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
         _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
@@ -148,7 +158,8 @@ def kda_verify(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, 
                gate, norm_w, lower_bound, scale, eps, f_b, accepted, rec_u=None, rec_kg=None,
                T=None, record=False, gate_mode=0, ahead=-1, stream=None):
     """One verify step over T = slots.shape[1] tokens unless given; see
-    kda_verify in include/kda.h."""
+    kda_verify in include/kda.h (an FP32 conv_state runs
+    kda_verify_f32conv)."""
     import torch
 
     if slots.dim() != 2:
@@ -168,7 +179,9 @@ def kda_verify(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, 
         if tuple(rec_u.shape) != (B, H, T, HEAD_DIM) or \
                 tuple(rec_kg.shape) != (B, H, T, 2 * HEAD_DIM):
             raise ValueError("rec_u / rec_kg: expected [B, H, T, 128] / [B, H, T, 256]")
-    status = load_library().kda_verify(
+    lib = load_library()
+    entry = lib.kda_verify_f32conv if conv_state.dtype == torch.float32 else lib.kda_verify
+    status = entry(
         _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
         _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
         _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b), _ptr(accepted),

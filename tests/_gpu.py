@@ -15,7 +15,7 @@ def to_device(p, device="cuda"):
     for k, v in p.items():
         if not isinstance(v, np.ndarray):
             d[k] = v
-        elif k in _BF16:
+        elif k in _BF16 and v.dtype == np.uint16:
             d[k] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to(device).view(torch.bfloat16)
         else:
             d[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)

@@ -66,8 +66,9 @@ def compare_step(before, ref, got, taps, items=None, report=None):
     `report` (a dict) with counts."""
     B, H, T = before["B"], before["H"], before["T"]
     rep = {} if report is None else report
-    # conv windows: exact bits everywhere
-    diff = np.nonzero(ref["conv_state"] != got["conv_state"])
+    # conv windows: exact bits everywhere (BF16 bits, or FP32 bits of an FP32 pool)
+    bits = np.uint32 if ref["conv_state"].dtype == np.float32 else np.uint16
+    diff = np.nonzero(ref["conv_state"].view(bits) != got["conv_state"].view(bits))
     assert diff[0].size == 0, f"conv_state differs at {len(diff[0])} places, first {[d[0] for d in diff]}"
     # state pages
     writes = written_targets(before)

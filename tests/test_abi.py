@@ -33,7 +33,8 @@ def declared():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert names == ["kda_decode", "kda_replay", "kda_status_string", "kda_validate", "kda_verify"]
+    assert names == ["kda_decode", "kda_decode_f32conv", "kda_replay", "kda_status_string",
+                     "kda_validate", "kda_verify", "kda_verify_f32conv"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -90,6 +91,18 @@ def test_entry_points_reject_before_device_work(lib):
     st = lib.kda_verify(*args, -5.0, 0.088, 1e-6, P(0x1000), P(0x1000), None, None,
                         4, 2, 40, 6, 4, 4, 1, 0, -1, None)
     assert st == NUL  # record without record buffers
+    # the FP32-pool entry points run the same checks
+    st = lib.kda_decode_f32conv(*args, -5.0, 0.088, 1e-6, P(0x1000), 4, 2, 5, 3, 2, -1, None)
+    assert st == GM
+    st = lib.kda_decode_f32conv(*args, -5.0, 0.088, 1e-6, P(0x1000), 4, 2, 5, 2, 0, -1, None)
+    assert st == SHP  # W < 3
+    for T, want in ((9, TOK), (1, TOK)):
+        st = lib.kda_verify_f32conv(*args, -5.0, 0.088, 1e-6, P(0x1000), P(0x1000), None, None,
+                                    4, 2, 40, 11, T, 9, 0, 0, -1, None)
+        assert st == want
+    st = lib.kda_verify_f32conv(*args, -5.0, 0.088, 1e-6, P(0x1000), P(0x1000), None, None,
+                                4, 2, 40, 6, 4, 4, 1, 0, -1, None)
+    assert st == NUL
 
 
 def test_replay_rejects_before_device_work(lib):

@@ -134,6 +134,35 @@ def test_conv_bias(gpu):
         check(gpu, p, f"bias T={T}")
 
 
+# --------------------------------------------------------------------------
+# FP32 convolution pool (kda_decode_f32conv / kda_verify_f32conv)
+
+
+@pytest.mark.parametrize("name", ["decode_b256", "verify_t4", "verify_record_t8"])
+def test_conv_f32_parity(gpu, name):
+    """Full-size workloads with the convolution pool in FP32 (taps not BF16
+    values): windows bit-exact, the rest under the same contract."""
+    p = inputs.make_problem(name, conv_f32=1)
+    assert p["conv_state"].dtype == np.float32
+    check(gpu, p, f"{name} conv_f32")
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_conv_f32_ragged_bias(gpu, T):
+    B, H = 5, 3
+    cfg = dict(B=B, H=H, T=T, N=B * T + 2, W=T + 3, seed=600 + T, conv_f32=1,
+               record=int(T == 8))
+    p = inputs.make_problem(cfg)
+    rng = np.random.default_rng(8)
+    p["conv_b"] = to_bf16(rng.standard_normal(3 * H * 128).astype(np.float32) * 0.3)
+    p["has_bias"] = 1
+    if T == 1:
+        p["slots"][2] = 0
+    else:
+        p["accepted"][1] = T + 1  # padding
+    check(gpu, p, f"conv_f32 bias T={T}")
+
+
 @pytest.mark.parametrize("name", ["decode_b64", "verify_t4", "verify_record_t8"])
 def test_prefetch_changes_nothing(gpu, name):
     """The prefetch distance is a hint: every value gives identical bits."""
