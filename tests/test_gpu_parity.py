@@ -375,3 +375,41 @@ def test_nondefault_stream(gpu):
         gpu.run(d, stream=s)
     s.synchronize()
     _parity.compare_step(before, ref, gpu.to_host(d), taps)
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture: a decode and a verify step recorded once, replayed
+
+
+def test_graph_capture_replays_match_eager(gpu):
+    """The entry points enqueue on the caller's stream and allocate nothing,
+    so a decode + verify pair can be captured in a HIP graph and replayed.
+    Every replay (with unrelated eager work and synchronisations between
+    them) must give the eager launches' bits."""
+    import torch
+
+    dec = inputs.make_problem("decode_b64")
+    ver = inputs.make_problem(dict(B=16, H=32, T=4, N=65, W=6, seed=41))
+    eager = [gpu.to_device(copy_problem(dec)), gpu.to_device(copy_problem(ver))]
+    graphed = [gpu.to_device(copy_problem(dec)), gpu.to_device(copy_problem(ver))]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for d in graphed:
+            gpu.run(d)
+    torch.cuda.synchronize()
+    for k in range(4):
+        say(f"[graph] replay {k}")
+        for d in eager:
+            gpu.run(d)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        scratch = torch.arange(1 << 20, device="cuda", dtype=torch.float32)
+        assert float(scratch.sum()) > 0
+        for e, r in zip(eager, graphed):
+            he, hr = gpu.to_host(e), gpu.to_host(r)
+            for key in ("state", "conv_state", "out"):
+                a, b = he[key], hr[key]
+                bits = np.uint32 if a.dtype == np.float32 else np.uint16
+                assert np.array_equal(a.view(bits), b.view(bits)), (k, key)
