@@ -39,15 +39,31 @@ __device__ __forceinline__ float round_bf16(float f) {
 
 // ---- the page's helpers --------------------------------------------------
 
+// exp and sigmoid on the hardware exp2 (v_exp_f32, 1 ulp) and reciprocal
+// (v_rcp_f32, 1 ulp): within |x|/2 + 2 FP32 ulps (exp; the argument's own
+// rounding grows with |x|) or a few ulps (sigmoid) of the correctly rounded
+// values.  Used where the result stays FP32 (beta, the decay, the output
+// gate), whose rounding order is free; the exact special values hold:
+// exp(0) = 1, sigmoid(+-large) = 1 or 0.
+__device__ __forceinline__ float exp_fast(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + exp_fast(-x));
+}
+
 // SiLU x / (1 + exp(-x)) as three FP32 operations (exp rounded to FP32, then
 // the add and the IEEE divide), stored BF16: the value the oracle defines.
-// Fast path: exp from v_exp_f32 (2^(-x log2 e)).  Its result y_f differs from
-// the value y_c of the exactly rounded steps by at most (1.5|x| + 10) FP32
-// ulps (argument rounding |x| 1.3e-7 relative, v_exp_f32 within 4 ulps, three
-// roundings), so when y_f is more than 2|x| + 16 ulps away from a BF16
-// rounding midpoint both round to the same BF16 value.  Otherwise, and for
-// |x| >= 80 (near exp over/underflow), the steps are redone with exp in FP64
-// rounded once to FP32.
+// Fast path: exp from v_exp_f32 (2^(-x log2 e)) and the quotient as
+// x * rcp(1 + e).  Its result y_f differs from the value y_c of the exactly
+// rounded steps by at most (1.5|x| + 12) FP32 ulps (argument rounding
+// 0.61|x| 2^-23 relative, v_exp_f32 and v_rcp_f32 within 4 and 1 ulps, the
+// roundings of the add and the product; a relative error r is at most
+// 2^24 r ulps of y), so when y_f is more than 2|x| + 16 ulps away from a
+// BF16 rounding midpoint both round to the same BF16 value.  Otherwise, and
+// for |x| >= 80 (near exp over/underflow), the steps are redone with exp in
+// FP64 rounded once to FP32 and an IEEE divide.
 __device__ __forceinline__ float silu_bf16_exact(float x) {
   const float e = static_cast<float>(exp(-static_cast<double>(x)));
   const float d = 1.0f + e;
@@ -57,7 +73,7 @@ __device__ __forceinline__ float silu_bf16_exact(float x) {
 __device__ __forceinline__ float silu_bf16(float x) {
   const float ax = fabsf(x);
   const float ef = __builtin_amdgcn_exp2f(x * -1.44269504088896341f);
-  const float yf = x / (1.0f + ef);
+  const float yf = x * __builtin_amdgcn_rcpf(1.0f + ef);
   const uint32_t bits = __float_as_uint(yf);
   const int dist = abs(static_cast<int>(bits & 0xffffu) - 0x8000);
   const int margin = static_cast<int>(2.0f * fminf(ax, 80.0f)) + 16;
@@ -65,12 +81,10 @@ __device__ __forceinline__ float silu_bf16(float x) {
   return silu_bf16_exact(x);
 }
 
-__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
-
 // exp(lower_bound * sigmoid(exp(A_log) * (raw_g + dt_bias))); e = exp(A_log).
 __device__ __forceinline__ float decay_f32(float e, float raw_g, float dt, float lower_bound) {
   const float y = e * (raw_g + dt);
-  return expf(lower_bound * sigmoid_f32(y));
+  return exp_fast(lower_bound * sigmoid_fast(y));
 }
 
 // ---- cross-lane reductions -----------------------------------------------

@@ -291,7 +291,7 @@ __device__ __forceinline__ void norms_beta(const Item& it, SH& sh, float beta_lo
       }
     }
   }
-  if (tid < T) sh.beta[tid] = sigmoid_f32(beta_logit);
+  if (tid < T) sh.beta[tid] = sigmoid_fast(beta_logit);
 }
 
 // Gate projection raw_g[t][f] = BF16(sum_j F_B[h*128+f][j] f_a[t][j]), exact:
@@ -485,7 +485,7 @@ __device__ __forceinline__ void gated_rmsnorm(const Args& A, const Item& it, SH&
     for (int t = 0; t < T; ++t) {
       const float variance = (sh.os[t][0] + sh.os[t][1]) * (1.0f / 128.0f) + A.eps;
       const float rstd = 1.0f / sqrtf(variance);
-      const float sg = sigmoid_f32(bf16_bits_to_f32(oo.gate[t]));
+      const float sg = sigmoid_fast(bf16_bits_to_f32(oo.gate[t]));
       const size_t idx = (it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + tid;
       A.out[idx] = static_cast<uint16_t>(f32_to_bf16_bits(((o[t][tid] * rstd) * oo.nw) * sg));
     }

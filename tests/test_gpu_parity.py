@@ -413,3 +413,63 @@ def test_graph_capture_replays_match_eager(gpu):
                 a, b = he[key], hr[key]
                 bits = np.uint32 if a.dtype == np.float32 else np.uint16
                 assert np.array_equal(a.view(bits), b.view(bits)), (k, key)
+
+
+def silu_inputs(n, rng):
+    """FP32 SiLU arguments: wide random magnitudes, tiny and large values,
+    and values whose SiLU lies within a few FP32 ulps of a BF16 rounding
+    midpoint (found by Newton steps in float64 from random midpoints)."""
+    parts = [rng.standard_normal(n // 5) * 3.0,
+             rng.uniform(-90.0, 90.0, n // 5),
+             np.sign(rng.standard_normal(n // 10)) * 10.0 ** rng.uniform(-38, 1.9, n // 10)]
+    # near-midpoint arguments
+    m = n - sum(len(q) for q in parts)
+    hb = rng.integers(0, 1 << 16, size=m).astype(np.uint32)
+    hb = hb[((hb & 0x7F80) != 0x7F80) & ((hb & 0x7F80) > 0x0000)]
+    lo = (hb << 16).view(np.float32).astype(np.float64)
+    spacing = 2.0 ** (np.floor(np.log2(np.abs(lo))) - 7)   # BF16 spacing at lo
+    mid = lo + np.sign(lo) * spacing / 2                  # halfway to the next BF16 value
+    ok = (mid > -0.278) & (np.abs(mid) < 80.0)             # SiLU's range
+    mid = mid[ok]
+    x = np.where(mid > 0, mid + 0.3, -0.5 + 0 * mid)
+    for _ in range(60):
+        e = np.exp(-x)
+        f = x / (1.0 + e) - mid
+        df = (1.0 + e + x * e) / (1.0 + e) ** 2
+        x = x - f / np.where(np.abs(df) < 1e-30, 1e-30, df)
+    x = x[np.isfinite(x)].astype(np.float32)
+    step = rng.integers(-3, 4, size=x.size).astype(np.int32)
+    x = (x.view(np.int32) + step).view(np.float32)
+    parts.append(x.astype(np.float64))
+    v = np.concatenate(parts).astype(np.float32)
+    return v[np.isfinite(v) & (np.abs(v) < 3.0e38)]
+
+
+def test_silu_fp32_inputs_gpu(gpu):
+    """The kernel's SiLU against the oracle's for ~2 M FP32 arguments,
+    including arguments whose SiLU sits next to a BF16 rounding midpoint:
+    an FP32 convolution pool with k tap weights [1, 0, 0, 0] makes the
+    convolution sum of token t the pool's tap t exactly, and record mode
+    stores BF16(silu(tap))."""
+    B, H, T = 1024, 8, 2
+    rng = np.random.default_rng(970)
+    p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=970, record=1,
+                                 conv_f32=1))
+    dim = H * 128
+    p["accepted"][:] = 1                       # window taps at columns 0, 1, 2
+    vals = silu_inputs(B * H * 128 * T, rng)
+    say(f"[silu32] {vals.size} FP32 inputs")
+    cs = p["slots"][:, 0]
+    k = np.resize(vals, B * H * 128 * T).reshape(B, H, 128, T)
+    pool = p["conv_state"]
+    for t in range(T):
+        pool[cs, dim:2 * dim, t] = k[..., t].reshape(B, dim)
+    p["conv_w"][1] = to_bf16(np.array([1, 0, 0, 0], np.float32))[:, None]
+    got = gpu_step(gpu, p)
+    k_gpu = got["rec_kg"][..., :128]                       # [B, H, T, 128]
+    xs = k.transpose(0, 1, 3, 2)                           # [B, H, T, 128]
+    # fma(tap, 1, +0) is the tap, except that -0 becomes +0
+    flat = (xs + np.float32(0.0)).reshape(-1)
+    want = to_bf16(np.array([oracle.silu_bf16(float(x)) for x in flat], dtype=np.float32))
+    bad = np.nonzero(k_gpu.reshape(-1) != want)[0]
+    assert bad.size == 0, f"{bad.size} SiLU mismatches, first x={flat[bad[0]]!r}"
