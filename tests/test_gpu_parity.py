@@ -473,3 +473,41 @@ def test_silu_fp32_inputs_gpu(gpu):
     want = to_bf16(np.array([oracle.silu_bf16(float(x)) for x in flat], dtype=np.float32))
     bad = np.nonzero(k_gpu.reshape(-1) != want)[0]
     assert bad.size == 0, f"{bad.size} SiLU mismatches, first x={flat[bad[0]]!r}"
+
+
+# --------------------------------------------------------------------------
+# slot tables wider than T, pools beyond 4 GiB
+
+
+def test_slot_stride_wider_than_tokens(gpu):
+    """slot_stride 7 for T = 4: the read slot is slots[b, accepted - 1] with
+    accepted <= 4, the write targets are the first 4 columns, and the pages
+    of columns 4-6 are untouched."""
+    B, H, T, S = 6, 4, 4, 7
+    p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * S + 1, W=T + 2, seed=1100, slot_stride=S))
+    assert p["slots"].shape == (B, S)
+    check(gpu, p, "slot_stride 7, T 4")
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_pool_beyond_4gib(gpu, T):
+    """A 4.4 GB state pool (2100 slots x 32 heads x 64 KiB) with the live
+    pages at the top slots, so every page offset exceeds 2^32 bytes; the
+    rest of the pool is zero and must stay so."""
+    B, H, N = 8, 32, 2100
+    small = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=1200 + T))
+    p = dict(small)
+    p["N"] = N
+    remap = np.zeros(small["N"], np.int32)
+    remap[1:] = np.arange(N - small["N"] + 1, N, dtype=np.int32)  # slot s -> N - small_N + s
+    p["slots"] = np.where(small["slots"] > 0, remap[np.maximum(small["slots"], 0)], small["slots"])
+    p["slots"] = np.ascontiguousarray(p["slots"].astype(np.int32))
+    state = np.zeros((N, H, 128, 128), np.float32)
+    state[remap[1:]] = small["state"][1:]
+    p["state"] = state
+    conv = np.zeros((N,) + small["conv_state"].shape[1:], small["conv_state"].dtype)
+    conv[remap[1:]] = small["conv_state"][1:]
+    p["conv_state"] = conv
+    assert (int(p["slots"].min()) * H) * 65536 >= 1 << 32
+    say(f"[4gib] T={T} pool {state.nbytes / 2**30:.1f} GiB")
+    check(gpu, p, f"pool beyond 4 GiB, T={T}")
