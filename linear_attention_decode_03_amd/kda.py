@@ -97,11 +97,22 @@ def _sizes(x, state, conv_state, T):
     return rows // T, H, N, conv_state.shape[2]
 
 
+def _gpu_device(state):
+    """The GPU the call runs on: that of the state pool.  Host tensors are
+    refused here, before any library call (their pointers are not device
+    memory)."""
+    import torch
+
+    if not isinstance(state, torch.Tensor) or state.device.type != "cuda":
+        raise ValueError("state: expected a tensor on a GPU (every operand is device memory)")
+    return state.device
+
+
 def _check_common(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
                   gate, norm_w, f_b, B, H, T):
     import torch
 
-    dev = state.device
+    dev = _gpu_device(state)
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     for name, t, dt, nd in (("x", x, bf, 2), ("conv_w", conv_w, bf, 3), ("conv_b", conv_b, bf, 1),
                             ("conv_state", conv_state, conv_state.dtype if conv_state.dtype in
@@ -126,12 +137,18 @@ def _check_common(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slot
         raise ValueError("slots: expected B rows")
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The hipStream_t handle: torch's current stream of `device` by default;
+    a torch stream must belong to `device`; an int is taken as a raw handle."""
     import torch
 
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(device).cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        if getattr(stream, "device", device) != device:
+            raise ValueError(f"stream: on {stream.device}, operands on {device}")
+        return stream.cuda_stream
+    return int(stream)
 
 
 def kda_decode(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
@@ -146,11 +163,12 @@ def kda_decode(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, 
                   gate, norm_w, f_b, B, H, 1)
     lib = load_library()
     entry = lib.kda_decode_f32conv if conv_state.dtype == torch.float32 else lib.kda_decode
-    status = entry(
-        _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
-        _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
-        _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
-        B, H, N, W, int(gate_mode), int(ahead), _stream(stream))
+    with torch.cuda.device(state.device):
+        status = entry(
+            _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
+            _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
+            _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
+            B, H, N, W, int(gate_mode), int(ahead), _stream(stream, state.device))
     _raise(status)
 
 
@@ -181,12 +199,13 @@ def kda_verify(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, 
             raise ValueError("rec_u / rec_kg: expected [B, H, T, 128] / [B, H, T, 256]")
     lib = load_library()
     entry = lib.kda_verify_f32conv if conv_state.dtype == torch.float32 else lib.kda_verify
-    status = entry(
-        _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
-        _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
-        _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b), _ptr(accepted),
-        _ptr(rec_u), _ptr(rec_kg), B, H, N, W, T, int(slots.shape[1]), int(bool(record)),
-        int(gate_mode), int(ahead), _stream(stream))
+    with torch.cuda.device(state.device):
+        status = entry(
+            _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
+            _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
+            _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
+            _ptr(accepted), _ptr(rec_u), _ptr(rec_kg), B, H, N, W, T, int(slots.shape[1]),
+            int(bool(record)), int(gate_mode), int(ahead), _stream(stream, state.device))
     _raise(status)
 
 
@@ -200,7 +219,7 @@ def kda_replay(rec_u, rec_kg, a_log, dt_bias, src_slots, dst_slots, n_tokens, st
     if rec_u.dim() != 4:
         raise ValueError("rec_u: expected [B, H, T, 128]")
     B, H, T = int(rec_u.shape[0]), int(rec_u.shape[1]), int(rec_u.shape[2])
-    dev = state.device
+    dev = _gpu_device(state)
     _check("rec_u", rec_u, torch.float32, 4, dev)
     _check("rec_kg", rec_kg, torch.bfloat16, 4, dev)
     _check("a_log", a_log, torch.float32, 1, dev)
@@ -216,10 +235,12 @@ def kda_replay(rec_u, rec_kg, a_log, dt_bias, src_slots, dst_slots, n_tokens, st
         raise ValueError("a_log / dt_bias: expected [H] / [H*128]")
     if state.shape[1] != H or tuple(state.shape[2:]) != (HEAD_DIM, HEAD_DIM):
         raise ValueError("state: expected [N, H, 128, 128]")
-    status = load_library().kda_replay(
-        _ptr(rec_u), _ptr(rec_kg), _ptr(a_log), _ptr(dt_bias), _ptr(src_slots), _ptr(dst_slots),
-        _ptr(n_tokens), _ptr(state), float(lower_bound), B, H, int(state.shape[0]), T,
-        _stream(stream))
+    lib = load_library()
+    with torch.cuda.device(dev):
+        status = lib.kda_replay(
+            _ptr(rec_u), _ptr(rec_kg), _ptr(a_log), _ptr(dt_bias), _ptr(src_slots),
+            _ptr(dst_slots), _ptr(n_tokens), _ptr(state), float(lower_bound), B, H,
+            int(state.shape[0]), T, _stream(stream, dev))
     _raise(status)
 
 

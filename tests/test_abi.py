@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from linear_attention_decode_03_amd import kda
@@ -123,3 +124,29 @@ def test_binding_raises_value_error(lib):
     with pytest.raises(RuntimeError):
         kda._raise(6)
     kda._raise(OK)
+
+
+def test_binding_refuses_host_tensors():
+    """Every operand is device memory: the binding refuses host tensors
+    before it calls the library (a host pointer would fault on the GPU)."""
+    import torch
+
+    from linear_attention_decode_03_amd import inputs
+
+    p = inputs.make_problem("tiny_decode")
+    t = {}
+    for k, v in p.items():
+        if isinstance(v, np.ndarray):
+            t[k] = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16) \
+                if v.dtype == np.uint16 else torch.from_numpy(v)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_decode(t["x"], t["conv_w"], None, t["conv_state"], t["f_a"], t["beta"],
+                       t["a_log"], t["dt_bias"], t["slots"], t["state"], t["out"], t["gate"],
+                       t["norm_w"], -5.0, 0.088, 1e-6, t["f_b"])
+    r = inputs.make_replay_problem(dict(B=2, H=2, T=2, N=5, seed=1))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_replay(torch.from_numpy(r["rec_u"]),
+                       torch.from_numpy(r["rec_kg"].view(np.int16)).view(torch.bfloat16),
+                       torch.from_numpy(r["a_log"]), torch.from_numpy(r["dt_bias"]),
+                       torch.from_numpy(r["src"]), torch.from_numpy(r["dst"]),
+                       torch.from_numpy(r["n"]), torch.from_numpy(r["state"]), -5.0)
