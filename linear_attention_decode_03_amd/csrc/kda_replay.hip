@@ -94,7 +94,7 @@ void kda_replay_kernel(const ReplayArgs R) {
   // 3. Apply the n tokens.
 #pragma unroll 1
   for (int t = 0; t < n; ++t) {
-    const float fk = 1.0f / sqrtf((sh_sq[t][0] + sh_sq[t][1]) + 1.0e-6f);
+    const float fk = __builtin_amdgcn_rsqf((sh_sq[t][0] + sh_sq[t][1]) + 1.0e-6f);
     float kh[8], a[8];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

@@ -460,8 +460,9 @@ __device__ __forceinline__ float load_dt(const Args& A, const Item& it) {
 
 template <int T, class SH>
 __device__ __forceinline__ void norm_factors(const SH& sh, int t, float& fq, float& fk) {
-  fq = 1.0f / sqrtf((sh.sq[t][0][0] + sh.sq[t][0][1]) + 1.0e-6f);
-  fk = 1.0f / sqrtf((sh.sq[t][1][0] + sh.sq[t][1][1]) + 1.0e-6f);
+  // v_rsq_f32 (1 ulp): the sums are >= 1e-6, normal numbers.
+  fq = __builtin_amdgcn_rsqf((sh.sq[t][0][0] + sh.sq[t][0][1]) + 1.0e-6f);
+  fk = __builtin_amdgcn_rsqf((sh.sq[t][1][0] + sh.sq[t][1][1]) + 1.0e-6f);
 }
 
 // ---- epilogue: gated RMSNorm --------------------------------------------------
@@ -484,7 +485,9 @@ __device__ __forceinline__ void gated_rmsnorm(const Args& A, const Item& it, SH&
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float variance = (sh.os[t][0] + sh.os[t][1]) * (1.0f / 128.0f) + A.eps;
-      const float rstd = 1.0f / sqrtf(variance);
+      // v_rsq_f32: 1 ulp for normal arguments (variance >= eps, 1e-6 in use);
+      // 0 and negative arguments give inf and NaN as 1 / sqrt would.
+      const float rstd = __builtin_amdgcn_rsqf(variance);
       const float sg = sigmoid_fast(bf16_bits_to_f32(oo.gate[t]));
       const size_t idx = (it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + tid;
       A.out[idx] = static_cast<uint16_t>(f32_to_bf16_bits(((o[t][tid] * rstd) * oo.nw) * sg));

@@ -232,7 +232,7 @@ void kda_record_kernel(const Args A) {
       const float qh = (sh.u.in.q[t][key] * fq) * A.scale;
       rt.W[t][key] = acc * kh;
       rt.W[T + t][key] = acc * qh;
-      rt.X[t][key] = kh / acc;
+      rt.X[t][key] = kh * __builtin_amdgcn_rcpf(acc);  // acc a normal number (bound above)
     }
 #pragma unroll
     for (int m = 2 * T; m < 16; ++m) rt.W[m][key] = 0.0f;
