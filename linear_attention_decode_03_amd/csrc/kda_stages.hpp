@@ -380,57 +380,86 @@ __device__ __forceinline__ void gate_mfma(const Args& A, const Item& it, SH& sh)
   }
 }
 
-// The same product from operands loaded in one round, so that they can be
-// issued ahead of the state page (record mode, where the page is loaded only
-// after the gate): lane (g, c) of wave w holds F_B rows 32w + 16 tile + c
-// and f_a row c (token c < T) at columns 32q + 8g .. +7, q < 4.  Same
-// accumulation chains and order as gate_mfma.
-struct GateMfmaOperands {
-  uint4 fb[2][4];
-  uint4 fa[4];
+// The same product on FP64 MFMA 4x4x4 (four 4x4 blocks per instruction, 16
+// cycles against 64 for 16x16x4): no padding columns when T is not a
+// multiple of 16, so half the cycles at T = 8 and a quarter at T <= 4.
+// Lane layout of the instruction: block b = (l >> 2) & 3; A: lane
+// 16k + 4b + i holds A[i][k]; B: lane 16k + 4b + j holds B[k][j]; D: lane
+// 16i + 4b + j holds D[i][j].  Block b = feature quad: A[i][k] =
+// F_B[32w + 16 fg + 4b + i][K], B[k][j] = f_a[4 tg + j][K] (the same in every
+// block), K = 32k + 8n + e at step (n, e); each D lane ends with a whole
+// sum.  Token groups (tg) past T - 1 load token T - 1 and are discarded.
+// The sums are exact in FP64, so the order changes no bit.
+template <int T>
+struct GateQuadOperands {
+  static constexpr int kTokenGroups = (T + 3) / 4;
+  uint4 fb[2][4];                 // [feature group fg][n]: 8 columns 32k + 8n ..
+  uint4 fa[kTokenGroups][4];      // [token group tg][n]
 };
 
+// F_B rows of feature group fg (the second group can be loaded once the
+// convolution operands are dead) and the f_a rows.
 template <int T>
-__device__ __forceinline__ void gate_mfma_load(const Args& A, const Item& it,
-                                               GateMfmaOperands& go) {
+__device__ __forceinline__ void gate_quad_load_fb(const Args& A, const Item& it,
+                                                  GateQuadOperands<T>& go, int fg) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
+  const int k = lane >> 4, b = (lane >> 2) & 3, i = lane & 3;
 #pragma unroll
-  for (int tile = 0; tile < 2; ++tile)
+  for (int n = 0; n < 4; ++n)
+    go.fb[fg][n] = *reinterpret_cast<const uint4*>(
+        A.f_b + (static_cast<size_t>(it.h) * kD + 32 * wave + 16 * fg + 4 * b + i) * kD +
+        32 * k + 8 * n);
+}
+
+template <int T>
+__device__ __forceinline__ void gate_quad_load_fa(const Args& A, const Item& it,
+                                                  GateQuadOperands<T>& go) {
+  const int lane = threadIdx.x & 63;
+  const int k = lane >> 4, j = lane & 3;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      go.fb[tile][q] = *reinterpret_cast<const uint4*>(
-          A.f_b + (static_cast<size_t>(it.h) * kD + 32 * wave + 16 * tile + c) * kD + 32 * q +
-          8 * g);
-  // Columns c >= T of the product are discarded, and column c of D depends
-  // only on column c of B: those lanes load token T - 1 instead of branching.
-  const int tok = c < T ? c : T - 1;
+  for (int tg = 0; tg < GateQuadOperands<T>::kTokenGroups; ++tg) {
+    const int tok = 4 * tg + j < T ? 4 * tg + j : T - 1;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    go.fa[q] = *reinterpret_cast<const uint4*>(A.f_a + (it.token0 + tok) * kD + 32 * q + 8 * g);
+    for (int n = 0; n < 4; ++n)
+      go.fa[tg][n] = *reinterpret_cast<const uint4*>(A.f_a + (it.token0 + tok) * kD + 32 * k +
+                                                     8 * n);
+  }
 }
 
 template <int T, class SH>
-__device__ __forceinline__ void gate_mfma_compute(const GateMfmaOperands& go, SH& sh) {
+__device__ __forceinline__ void gate_quad_compute(const GateQuadOperands<T>& go, SH& sh) {
+  constexpr int kTG = GateQuadOperands<T>::kTokenGroups;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
+  const int i = lane >> 4, b = (lane >> 2) & 3, j = lane & 3;
+  // Steps outside, (fg, tg) inside: each converted operand is used at once,
+  // and the 2 kTG accumulators are independent chains.
+  double acc[2][kTG];
 #pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
-    const int f0 = 32 * wave + 16 * tile;
-    f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+  for (int fg = 0; fg < 2; ++fg)
 #pragma unroll
-    for (int q0 = 0; q0 < 4; q0 += 2)
+    for (int tg = 0; tg < kTG; ++tg) acc[fg][tg] = 0.0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+  for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-              static_cast<double>(bf16_at(go.fb[tile][q0 + j], e)),
-              static_cast<double>(bf16_at(go.fa[q0 + j], e)), acc[j], 0, 0, 0);
-    if (c < T) {
+    for (int e = 0; e < 8; ++e) {
+      double bv[kTG];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sh.u.in.g[c][f0 + g + 4 * r] = static_cast<float>(acc[0][r] + acc[1][r]);
+      for (int tg = 0; tg < kTG; ++tg) bv[tg] = static_cast<double>(bf16_at(go.fa[tg][n], e));
+#pragma unroll
+      for (int fg = 0; fg < 2; ++fg) {
+        const double av = static_cast<double>(bf16_at(go.fb[fg][n], e));
+#pragma unroll
+        for (int tg = 0; tg < kTG; ++tg)
+          acc[fg][tg] = __builtin_amdgcn_mfma_f64_4x4x4f64(av, bv[tg], acc[fg][tg], 0, 0, 0);
+      }
+    }
+#pragma unroll
+  for (int fg = 0; fg < 2; ++fg) {
+    const int f = 32 * wave + 16 * fg + 4 * b + i;
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg) {
+      const int t = 4 * tg + j;
+      if (t < T) sh.u.in.g[t][f] = static_cast<float>(acc[fg][tg]);
     }
   }
 }

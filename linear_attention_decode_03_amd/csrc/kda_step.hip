@@ -180,25 +180,28 @@ void kda_record_kernel(const Args A) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
 
-  // 1. Every input operand in one round (loads of a wave retire in issue
-  //    order, so nothing that the prologue needs may queue behind the page).
-  //    The scheduling barriers keep the three groups in this order.
+  // 1. The input operands ahead of the state page (loads of a wave retire in
+  //    issue order, so nothing that the prologue needs may queue behind the
+  //    page): convolution, gate rows, f_a, beta, dt_bias; the output-norm
+  //    operands after the gate.  The scheduling barriers keep the groups in
+  //    this order.
   ConvOperands<T> co;
   conv_load<T, kBias, kConvF32>(A, it, co);
   __builtin_amdgcn_sched_barrier(0);
-  GateMfmaOperands go;
-  gate_mfma_load<T>(A, it, go);
+  GateQuadOperands<T> go;
+  gate_quad_load_fb<T>(A, it, go, 0);
+  gate_quad_load_fb<T>(A, it, go, 1);
+  gate_quad_load_fa<T>(A, it, go);
   const float beta_logit = load_beta<T>(A, it);
   const float dt = load_dt(A, it);
-  __builtin_amdgcn_sched_barrier(0);
-  OutputOperands<T> oo;
-  load_output_operands<T>(A, it, oo);
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. Convolution, norms, gate projection.
   conv_compute<T, true, kConvF32>(A, it, sh, co);
   norms_beta<T>(it, sh, beta_logit);
-  gate_mfma_compute<T>(go, sh);
+  gate_quad_compute<T>(go, sh);
+  OutputOperands<T> oo;
+  load_output_operands<T>(A, it, oo);
   __syncthreads();
 
   // 3. S0 into the MFMA B-operand layout: [tile][q] = rows 32w + 16 tile + c,
