@@ -45,22 +45,27 @@ void kda_replay_kernel(const ReplayArgs R) {
   const int lane_off = (row0 * kD + 4 * c16) * 4;
   const size_t rec0 = (static_cast<size_t>(b) * R.H + h) * R.T;
 
-  // 1. Records first (threads 0-127: k and raw_g of channel tid; 128-255: u
-  //    of row tid - 128), then the checkpoint page.
-  const int c = tid & (kD - 1);
-  uint16_t kraw[kMaxT], graw[kMaxT];
-  float uval[kMaxT];
+  // 1. Records first, then the checkpoint page.  Thread (half = tid >> 7,
+  //    channel c) takes tokens half, half + 2, ...: the k and raw_g of
+  //    channel c and the u of value row c.  No load sits under a branch (the
+  //    compiler would wait for each inside it, one round trip per token):
+  //    tokens past n - 1 load token n - 1 again, which stays inside the
+  //    record buffers, and are not used.  One value per register.
+  constexpr int kPer = kMaxT / 2;
+  const int c = tid & (kD - 1), half = tid >> 7;
+  const int t_last = n > 0 ? n - 1 : 0;
+  uint32_t kraw[kPer], graw[kPer];
+  float uval[kPer];
 #pragma unroll
-  for (int t = 0; t < kMaxT; ++t) {
-    if (t < n) {
-      if (tid < kD) {
-        kraw[t] = R.rec_kg[(rec0 + t) * (2 * kD) + c];
-        graw[t] = R.rec_kg[(rec0 + t) * (2 * kD) + kD + c];
-      } else {
-        uval[t] = R.rec_u[(rec0 + t) * kD + c];
-      }
-    }
+  for (int m = 0; m < kPer; ++m) {
+    const int t = 2 * m + half;
+    const size_t rec = rec0 + (t < t_last ? t : t_last);
+    kraw[m] = R.rec_kg[rec * (2 * kD) + c];
+    graw[m] = R.rec_kg[rec * (2 * kD) + kD + c];
+    uval[m] = R.rec_u[rec * kD + c];
   }
+  const float dt = R.dt_bias[static_cast<size_t>(h) * kD + c];
+  __builtin_amdgcn_sched_barrier(0);  // every record load ahead of the page
   float4 st[8][2];
   {
     const __amdgpu_buffer_rsrc_t page = page_rsrc(R.state, src, h, R.H);
@@ -70,24 +75,20 @@ void kda_replay_kernel(const ReplayArgs R) {
       for (int j = 0; j < 2; ++j) st[i][j] = load_f4(page, lane_off, i * kD * 4 + j * 256);
   }
 
-  // 2. k, decay and u tables; per-token sums of squares of k.
-  if (tid < kD) {
-    const float e = expf(R.a_log[h]);
-    const float dt = R.dt_bias[static_cast<size_t>(h) * kD + c];
+  // 2. k, decay and u tables; per-token sums of squares of k (the two waves
+  //    of a half hold channels 0-63 and 64-127).
+  const float e = expf(R.a_log[h]);
 #pragma unroll
-    for (int t = 0; t < kMaxT; ++t) {
-      if (t < n) {
-        const float k = bf16_bits_to_f32(kraw[t]);
-        sh_k[t][c] = k;
-        sh_a[t][c] = decay_f32(e, bf16_bits_to_f32(graw[t]), dt, R.lower_bound);
-        const float sk = wave_sum(k * k);
-        if (lane == 0) sh_sq[t][wave] = sk;
-      }
+  for (int m = 0; m < kPer; ++m) {
+    const int t = 2 * m + half;
+    if (t < n) {
+      const float k = bf16_bits_to_f32(kraw[m]);
+      sh_k[t][c] = k;
+      sh_a[t][c] = decay_f32(e, bf16_bits_to_f32(graw[m]), dt, R.lower_bound);
+      sh_u[t][c] = uval[m];
+      const float sk = wave_sum(k * k);
+      if (lane == 0) sh_sq[t][wave & 1] = sk;
     }
-  } else {
-#pragma unroll
-    for (int t = 0; t < kMaxT; ++t)
-      if (t < n) sh_u[t][c] = uval[t];
   }
   __syncthreads();
 
