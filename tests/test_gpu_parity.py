@@ -511,3 +511,48 @@ def test_pool_beyond_4gib(gpu, T):
     assert (int(p["slots"].min()) * H) * 65536 >= 1 << 32
     say(f"[4gib] T={T} pool {state.nbytes / 2**30:.1f} GiB")
     check(gpu, p, f"pool beyond 4 GiB, T={T}")
+
+
+# --------------------------------------------------------------------------
+# a seeded sweep of small random configurations over every axis
+
+
+def random_configs(n=36, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(1, 9))
+        B = int(rng.integers(1, 9))
+        H = int(rng.choice([1, 2, 3, 5, 7, 8, 12]))
+        record = int(T > 1 and rng.random() < 0.35)
+        stride = T if T == 1 else T + int(rng.integers(0, 3))
+        W = (3 if T == 1 else T + 2) + int(rng.integers(0, 3))
+        cfg = dict(B=B, H=H, T=T, W=W, seed=3000 + i, record=record,
+                   gate_mode=int(rng.integers(0, 2)), conv_f32=int(rng.random() < 0.3),
+                   lower_bound=float(rng.choice([-5.0, -5.0, -1.0, -9.5, -12.0, 0.0])))
+        if T > 1:
+            cfg["slot_stride"] = stride
+            cfg["N"] = B * stride + 1 + int(rng.integers(0, 5))
+        else:
+            cfg["N"] = B + 1 + int(rng.integers(0, 5))
+        out.append((cfg, bool(rng.random() < 0.3), bool(rng.random() < 0.3)))
+    return out
+
+
+@pytest.mark.parametrize("k", range(36))
+def test_random_small_configs(gpu, k):
+    cfg, bias, pad = random_configs()[k]
+    p = inputs.make_problem(cfg)
+    rng = np.random.default_rng(cfg["seed"])
+    if bias:
+        p["conv_b"] = to_bf16(rng.standard_normal(3 * p["H"] * 128).astype(np.float32) * 0.3)
+        p["has_bias"] = 1
+    if pad and p["B"] > 1:
+        b = int(rng.integers(0, p["B"]))
+        if p["T"] == 1:
+            p["slots"][b] = 0
+        else:
+            p["accepted"][b] = 0
+            if p["B"] > 2:       # and a skipped write target elsewhere
+                p["slots"][(b + 1) % p["B"], p["T"] - 1] = 0
+    check(gpu, p, f"random {k}: {cfg} bias={bias} pad={pad}")
