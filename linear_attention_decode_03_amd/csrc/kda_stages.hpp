@@ -60,7 +60,7 @@ struct Shared {
   float v[T][kD];
   float o[kRecordBody ? 1 : T][kD];  // token-by-token body's outputs
   float beta[kMaxT];
-  float sq[T][2][2];  // [token][q, k][wave 0, 1]
+  float sq[T][2];     // [token][q, k]: sums of squares
   float os[T][2];     // [token][wave 0, 1]
 };
 
@@ -174,20 +174,31 @@ __device__ __forceinline__ void load_output_operands(const Args& A, const Item& 
 
 // ---- prologue: convolution, SiLU, norms, gate projection, decay -------------
 
-// Convolution + SiLU.  Threads 0-127 make q and k of channel tid, threads
-// 128-255 make v of channel tid - 128.  Split in two so that the operand
-// loads can be issued before the state page: loads of a wave retire in issue
-// order, so inputs loaded after the page could not be used before all of it
-// has arrived.
+// Convolution + SiLU.  Wave w < 3 makes part w of the q | k | v channels,
+// lane l channels 2l and 2l + 1 of the head: inputs, weights and bias arrive
+// as one 4-byte pair per lane.  Every operand load is issued unconditionally
+// (the compiler waits for a load under a branch inside the branch) and ahead
+// of the state page (loads of a wave retire in issue order, so an input
+// loaded after the page could not be used before all of the page has
+// arrived).  Wave 3 therefore issues the same loads as wave 2 and uses none
+// of them: a window column must be read and rewritten by one wave only, as
+// another wave's read could land after the rewrite.  Waves 0 and 1 hold all
+// of q and all of k and reduce their sums of squares alone.
 template <int T>
 struct ConvOperands {
-  // [part slot][tap0, tap1, tap2, x_0 .. x_{T-1}]: taps in the pool's type
-  // (BF16 or FP32 bits), inputs as BF16 bits, one per register: packing two
-  // into one would consume each load as it is issued.
-  uint32_t raw[2][3 + T];
-  uint32_t w[2][4];   // BF16 bits of the four taps' weights
-  uint32_t bias[2];   // BF16 bits of the bias (0: none)
+  uint32_t tap[2][3];  // [channel 2l, 2l + 1][tap]: the pool's type (BF16 or FP32 bits)
+  uint32_t x[T];       // BF16 pair of each token's input (low half: channel 2l)
+  uint32_t w[4];       // BF16 pair of each tap's weight
+  uint32_t bias;       // BF16 pair of the bias (0: none)
 };
+
+__device__ __forceinline__ int conv_wave() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+}
+
+__device__ __forceinline__ uint32_t load_pair(const uint16_t* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
 
 template <bool kConvF32>
 __device__ __forceinline__ float tap_value(uint32_t bits) {
@@ -196,79 +207,89 @@ __device__ __forceinline__ float tap_value(uint32_t bits) {
 
 template <int T, bool kBias, bool kConvF32>
 __device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOperands<T>& co) {
-  const int tid = threadIdx.x;
-  const int c = tid & (kD - 1);
-  const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 7) != 0;  // wave-uniform
+  const int wave = conv_wave();
+  const int part = wave < 2 ? wave : 2;
+  const size_t hc = static_cast<size_t>(it.h) * kD + 2 * (threadIdx.x & 63);
+  const size_t ch = static_cast<size_t>(part) * it.dim + hc;
+  const size_t base = (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W + it.off;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (s == 1 && v_wave) break;
-    const int part = v_wave ? 2 : s;
-    const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
-    const size_t base = (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W + it.off;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      co.raw[s][i] = kConvF32 ? static_cast<const uint32_t*>(A.conv_state)[base + i]
-                              : static_cast<const uint16_t*>(A.conv_state)[base + i];
+    for (int i = 0; i < 3; ++i) {
+      const size_t at = base + static_cast<size_t>(j) * A.W + i;
+      co.tap[j][i] = kConvF32 ? static_cast<const uint32_t*>(A.conv_state)[at]
+                              : static_cast<const uint16_t*>(A.conv_state)[at];
+    }
 #pragma unroll
-    for (int t = 0; t < T; ++t) co.raw[s][3 + t] = A.x[(it.token0 + t) * 3 * it.dim + ch];
+  for (int t = 0; t < T; ++t) co.x[t] = load_pair(A.x + (it.token0 + t) * 3 * it.dim + ch);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      co.w[s][i] = A.conv_w[(static_cast<size_t>(part) * 4 + i) * it.dim +
-                            static_cast<size_t>(it.h) * kD + c];
-    co.bias[s] = kBias ? A.conv_b[ch] : 0u;
-  }
+  for (int i = 0; i < 4; ++i)
+    co.w[i] = load_pair(A.conv_w + (static_cast<size_t>(part) * 4 + i) * it.dim + hc);
+  co.bias = kBias ? load_pair(A.conv_b + ch) : 0u;
 }
 
 // The window is rewritten in place after it was read: [tap1, tap2, x_0 ..]
-// in the pool's type (an FP32 pool receives the inputs' exact FP32 values);
-// record mode stores k.
+// in the pool's type (an FP32 pool receives the inputs' exact FP32 values).
+// The outputs go to the q, k and v tables; record mode stores k.
 template <int T, bool kRecord, bool kConvF32, class SH>
 __device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& sh,
                                              const ConvOperands<T>& co) {
-  const int tid = threadIdx.x;
-  const int c = tid & (kD - 1);
-  const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 7) != 0;  // wave-uniform
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (s == 1 && v_wave) break;
-    const int part = v_wave ? 2 : s;
-    const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + c;
+  const int part = conv_wave();
+  if (part == 3) return;  // issued copies of wave 2's loads only
+  const int lane = threadIdx.x & 63;
+  const size_t hc = static_cast<size_t>(it.h) * kD + 2 * lane;
+  const size_t ch = static_cast<size_t>(part) * it.dim + hc;
+  {
     const size_t base = (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
-    if constexpr (kConvF32) {
-      uint32_t* col = static_cast<uint32_t*>(A.conv_state) + base;
-      col[0] = co.raw[s][1];
-      col[1] = co.raw[s][2];
 #pragma unroll
-      for (int t = 0; t < T; ++t) col[2 + t] = co.raw[s][3 + t] << 16;
-    } else {
-      uint16_t* col = static_cast<uint16_t*>(A.conv_state) + base;
-      col[0] = static_cast<uint16_t>(co.raw[s][1]);
-      col[1] = static_cast<uint16_t>(co.raw[s][2]);
+    for (int j = 0; j < 2; ++j) {
+      const size_t at = base + static_cast<size_t>(j) * A.W;
+      if constexpr (kConvF32) {
+        uint32_t* col = static_cast<uint32_t*>(A.conv_state) + at;
+        col[0] = co.tap[j][1];
+        col[1] = co.tap[j][2];
 #pragma unroll
-      for (int t = 0; t < T; ++t) col[2 + t] = static_cast<uint16_t>(co.raw[s][3 + t]);
+        for (int t = 0; t < T; ++t) col[2 + t] = j ? co.x[t] & 0xffff0000u : co.x[t] << 16;
+      } else {
+        uint16_t* col = static_cast<uint16_t*>(A.conv_state) + at;
+        col[0] = static_cast<uint16_t>(co.tap[j][1]);
+        col[1] = static_cast<uint16_t>(co.tap[j][2]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) col[2 + t] = static_cast<uint16_t>(j ? co.x[t] >> 16 : co.x[t]);
+      }
     }
-    float* dst = part == 0 ? &sh.u.in.q[0][0] : part == 1 ? &sh.u.in.k[0][0] : &sh.v[0][0];
+  }
+  float* dst = part == 0 ? &sh.u.in.q[0][0] : part == 1 ? &sh.u.in.k[0][0] : &sh.v[0][0];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float acc = bf16_bits_to_f32(co.bias[s]);
+  for (int t = 0; t < T; ++t) {
+    float y[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float acc = j ? bf16_hi(co.bias) : bf16_lo(co.bias);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t r = co.raw[s][t + i];
-        const float term = t + i < 3 ? tap_value<kConvF32>(r) : bf16_bits_to_f32(r);
-        acc = fmaf(term, bf16_bits_to_f32(co.w[s][i]), acc);
+        const int r = t + i;  // window position: taps 0-2, then the inputs
+        const float term = r < 3 ? tap_value<kConvF32>(co.tap[j][r < 3 ? r : 0])
+                                 : (j ? bf16_hi(co.x[r < 3 ? 0 : r - 3])
+                                      : bf16_lo(co.x[r < 3 ? 0 : r - 3]));
+        acc = fmaf(term, j ? bf16_hi(co.w[i]) : bf16_lo(co.w[i]), acc);
       }
-      const float y = silu_bf16(acc);
-      dst[t * kD + c] = y;
-      if constexpr (kRecord) {
-        if (part == 1)
-          A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + c] =
-              static_cast<uint16_t>(f32_to_bf16_bits(y));
-      }
+      y[j] = silu_bf16(acc);
+    }
+    *reinterpret_cast<float2*>(&dst[t * kD + 2 * lane]) = make_float2(y[0], y[1]);
+    if (part < 2) {
+      const float ss = wave_sum(fmaf(y[1], y[1], y[0] * y[0]));
+      if (lane == 0) sh.sq[t][part] = ss;
+    }
+    if constexpr (kRecord) {
+      if (part == 1)
+        *reinterpret_cast<uint32_t*>(
+            &A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + 2 * lane]) =
+            f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
     }
   }
 }
 
-// Sums of squares of q and k (waves 0 and 1 hold channels 0-63, 64-127) and
 // beta = sigmoid(logit).  The logit of token tid (tid < T) is loaded by
 // load_beta with the other input operands, ahead of the state page.
 template <int T>
@@ -278,20 +299,8 @@ __device__ __forceinline__ float load_beta(const Args& A, const Item& it) {
 }
 
 template <int T, class SH>
-__device__ __forceinline__ void norms_beta(const Item& it, SH& sh, float beta_logit) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (wave < 2) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float q = sh.u.in.q[t][tid], k = sh.u.in.k[t][tid];
-      const float sq = wave_sum(q * q), sk = wave_sum(k * k);
-      if (lane == 0) {
-        sh.sq[t][0][wave] = sq;
-        sh.sq[t][1][wave] = sk;
-      }
-    }
-  }
-  if (tid < T) sh.beta[tid] = sigmoid_fast(beta_logit);
+__device__ __forceinline__ void store_beta(SH& sh, float beta_logit) {
+  if (threadIdx.x < T) sh.beta[threadIdx.x] = sigmoid_fast(beta_logit);
 }
 
 // Gate projection raw_g[t][f] = BF16(sum_j F_B[h*128+f][j] f_a[t][j]), exact:
@@ -490,8 +499,8 @@ __device__ __forceinline__ float load_dt(const Args& A, const Item& it) {
 template <int T, class SH>
 __device__ __forceinline__ void norm_factors(const SH& sh, int t, float& fq, float& fk) {
   // v_rsq_f32 (1 ulp): the sums are >= 1e-6, normal numbers.
-  fq = __builtin_amdgcn_rsqf((sh.sq[t][0][0] + sh.sq[t][0][1]) + 1.0e-6f);
-  fk = __builtin_amdgcn_rsqf((sh.sq[t][1][0] + sh.sq[t][1][1]) + 1.0e-6f);
+  fq = __builtin_amdgcn_rsqf(sh.sq[t][0] + 1.0e-6f);
+  fk = __builtin_amdgcn_rsqf(sh.sq[t][1] + 1.0e-6f);
 }
 
 // ---- epilogue: gated RMSNorm --------------------------------------------------

@@ -83,7 +83,7 @@ void kda_step_kernel(const Args A) {
   // 2. Inputs.
   conv_compute<T, kRecord, kConvF32>(A, it, sh, co);
   if constexpr (T == 1) beta_logit = load_beta<T>(A, it);
-  norms_beta<T>(it, sh, beta_logit);
+  store_beta<T>(sh, beta_logit);
   if constexpr (T == 1) gate_valu(go, sh); else gate_mfma<T>(A, it, sh);
   __syncthreads();
   if constexpr (T == 1) dt = load_dt(A, it);
@@ -198,7 +198,7 @@ void kda_record_kernel(const Args A) {
 
   // 2. Convolution, norms, gate projection.
   conv_compute<T, true, kConvF32>(A, it, sh, co);
-  norms_beta<T>(it, sh, beta_logit);
+  store_beta<T>(sh, beta_logit);
   gate_quad_compute<T>(go, sh);
   OutputOperands<T> oo;
   load_output_operands<T>(A, it, oo);
