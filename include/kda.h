@@ -30,6 +30,11 @@
  *   - `state` and `conv_state` are updated in place; `out`, `rec_u` and
  *     `rec_kg` are written; everything else is read only.  `out`, `rec_u`
  *     and `rec_kg` must not alias any input.
+ *   - Alignment: state, f_a and f_b on 16 bytes (16-byte vector accesses);
+ *     x, conv_w, conv_b and rec_kg on 4 bytes (BF16 channel pairs moved as
+ *     one 32-bit word); every other operand on its element size.  Tensors
+ *     from a device allocator (and their row slices) satisfy this; a call
+ *     that does not returns KDA_ERR_ALIGN.
  *   - Errors: on any non-OK status nothing is enqueued, except KDA_ERR_LAUNCH
  *     (the launch itself failed).  B = 0 is a successful no-op.
  *   - Caller contract, not checked on the device: the live read slots and
@@ -59,7 +64,9 @@ typedef enum kda_status {
   KDA_ERR_NULL = 4,       /* a required pointer is NULL */
   KDA_ERR_SHAPE = 5,      /* B < 0, H < 1, N < 1, W too small, slot_stride < T,
                              non-finite scalar, or sizes beyond 32-bit grids */
-  KDA_ERR_LAUNCH = 6      /* the kernel launch failed (hipGetLastError) */
+  KDA_ERR_LAUNCH = 6,     /* the kernel launch failed (hipGetLastError) */
+  KDA_ERR_ALIGN = 7       /* a pointer not aligned as its operand needs (see the
+                             alignment convention above) */
 } kda_status;
 
 /*
@@ -185,6 +192,7 @@ kda_status kda_verify_f32conv(const uint16_t* x, const uint16_t* conv_w,
  * [0, T] is skipped (nothing is written for it).  Caller contract: the dst
  * slots are distinct across requests and no dst is another request's src.
  * Status: KDA_ERR_TOKENS for T outside [1, 8]; KDA_ERR_SHAPE, KDA_ERR_NULL,
+ * KDA_ERR_ALIGN (state on 16 bytes, the rest on their element size),
  * KDA_ERR_LAUNCH as for the other entry points.
  */
 kda_status kda_replay(const float* rec_u, const uint16_t* rec_kg, const float* a_log,

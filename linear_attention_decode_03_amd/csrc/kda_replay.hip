@@ -136,6 +136,14 @@ kda_status kda_replay(const float* rec_u, const uint16_t* rec_kg, const float* a
   if (B == 0) return KDA_OK;
   if (!rec_u || !rec_kg || !a_log || !dt_bias || !src_slots || !dst_slots || !n_tokens || !state)
     return KDA_ERR_NULL;
+  // 16-byte page loads and stores; the element size for everything else.
+  const auto misaligned = [](const void* p, uintptr_t bytes) {
+    return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) != 0;
+  };
+  if (misaligned(state, 16) || misaligned(rec_u, 4) || misaligned(rec_kg, 2) ||
+      misaligned(a_log, 4) || misaligned(dt_bias, 4) || misaligned(src_slots, 4) ||
+      misaligned(dst_slots, 4) || misaligned(n_tokens, 4))
+    return KDA_ERR_ALIGN;
   ReplayArgs R;
   R.rec_u = rec_u; R.rec_kg = rec_kg; R.a_log = a_log; R.dt_bias = dt_bias;
   R.src = src_slots; R.dst = dst_slots; R.n = n_tokens; R.state = state;

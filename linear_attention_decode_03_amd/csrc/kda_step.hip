@@ -306,6 +306,10 @@ void kda_record_kernel(const Args A) {
 
 // ---- host side -------------------------------------------------------------
 
+bool misaligned(const void* p, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) != 0;
+}
+
 kda_status check(const Args& A, int T, int record, int gate_mode) {
   if (T < 1 || T > kMaxT) return KDA_ERR_TOKENS;
   if (gate_mode != 0 && gate_mode != 1) return KDA_ERR_GATE_MODE;
@@ -323,6 +327,17 @@ kda_status check(const Args& A, int T, int record, int gate_mode) {
     return KDA_ERR_NULL;
   if (T > 1 && !A.accepted) return KDA_ERR_NULL;
   if (record && (!A.rec_u || !A.rec_kg)) return KDA_ERR_NULL;
+  // Alignment the kernels' accesses assume: 16 bytes for the state pool and
+  // the gate projection operands (16-byte loads), 4 bytes for the BF16
+  // operands moved as channel pairs, the element size for everything else.
+  if (misaligned(A.state, 16) || misaligned(A.f_a, 16) || misaligned(A.f_b, 16) ||
+      misaligned(A.x, 4) || misaligned(A.conv_w, 4) || misaligned(A.conv_b, 4) ||
+      misaligned(A.conv_state, A.conv_f32 ? 4 : 2) || misaligned(A.beta, 2) ||
+      misaligned(A.a_log, 4) || misaligned(A.dt_bias, 4) || misaligned(A.slots, 4) ||
+      misaligned(A.out, 2) || misaligned(A.gate, 2) || misaligned(A.norm_w, 2) ||
+      (T > 1 && misaligned(A.accepted, 4)) ||
+      (record && (misaligned(A.rec_u, 4) || misaligned(A.rec_kg, 4))))
+    return KDA_ERR_ALIGN;
   return KDA_OK;
 }
 
@@ -511,6 +526,7 @@ const char* kda_status_string(kda_status status) {
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "invalid sizes or scalars";
     case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_ALIGN: return "a pointer is not aligned as its operand needs";
   }
   return "unknown status";
 }

@@ -3,9 +3,10 @@
 Argument marshalling only: every step of the KDA decode / verify computation
 runs in the HIP kernels of the library.  Operands are torch tensors on the
 GPU (PyTorch provides device memory and streams); BF16 operands are
-torch.bfloat16 tensors.  Status codes 1-5 raise ValueError, like the
-constructor checks of the KdaWide class on the vLLM kda.wide page; code 6
-raises RuntimeError.  If the built library is missing the binding raises: it
+torch.bfloat16 tensors.  Argument errors (status codes 1-5, and 7 for a
+misaligned operand) raise ValueError, like the constructor checks of the
+KdaWide class on the vLLM kda.wide page; code 6 (launch) raises
+RuntimeError.  If the built library is missing the binding raises: it
 has no fallback of any kind.
 """
 
@@ -19,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 HEAD_DIM = 128
 
 KDA_OK, KDA_ERR_TOKENS, KDA_ERR_GATE_MODE, KDA_ERR_RECORD_T1, KDA_ERR_NULL, KDA_ERR_SHAPE, \
-    KDA_ERR_LAUNCH = range(7)
+    KDA_ERR_LAUNCH, KDA_ERR_ALIGN = range(8)
 
 _lib = None
 _P = ctypes.c_void_p

@@ -41,13 +41,13 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         s = kda.kda_status_string(code)
         assert s and s != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
 
 
-OK, TOK, GM, REC, NUL, SHP = 0, 1, 2, 3, 4, 5
+OK, TOK, GM, REC, NUL, SHP, ALN = 0, 1, 2, 3, 4, 5, 7
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -71,6 +71,28 @@ OK, TOK, GM, REC, NUL, SHP = 0, 1, 2, 3, 4, 5
     (dict(B=4, H=2, N=5, W=3, T=1, eps=float("nan")), SHP),
     (dict(B=4, H=2, N=5, W=3, T=1, lower_bound=float("inf")), SHP),
     (dict(B=1 << 20, H=1 << 12, N=5, W=3, T=1), SHP),            # grid beyond 2^31 items
+    # alignment: 16 bytes for state, f_a, f_b; 4 for x, conv_w, conv_b, rec_kg
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"state": 0x1008}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"f_a": 0x1004}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"f_b": 0x1002}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"x": 0x1002}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"conv_w": 0x1002}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"conv_b": 0x1002}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"beta": 0x1001}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"a_log": 0x1002}), ALN),
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"out": 0x1001}), ALN),
+    (dict(B=4, H=2, N=5, W=6, T=4, slot_stride=4, pointers={"accepted": 0x1002}), ALN),
+    (dict(B=4, H=2, N=5, W=6, T=4, slot_stride=4, record=1, pointers={"rec_kg": 0x1002}), ALN),
+    (dict(B=4, H=2, N=5, W=6, T=4, slot_stride=4, record=1, pointers={"rec_u": 0x1002}), ALN),
+    # what needs no more than its element size
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"state": 0x1010, "f_a": 0x1030, "beta": 0x1002,
+                                               "gate": 0x1002, "norm_w": 0x1002, "out": 0x1002,
+                                               "conv_state": 0x1002, "x": 0x1004}), OK),
+    # unused operands are not checked: accepted at T = 1, records without record
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"accepted": 0x1001}), OK),
+    (dict(B=4, H=2, N=5, W=6, T=4, slot_stride=4, pointers={"rec_kg": 0x1001}), OK),
+    # NULL is reported before alignment
+    (dict(B=4, H=2, N=5, W=3, T=1, pointers={"state": 0, "f_a": 0x1004}), NUL),
 ])
 def test_validate_codes(lib, kw, want):
     assert kda.kda_validate(**kw) == want
@@ -116,6 +138,12 @@ def test_replay_rejects_before_device_work(lib):
     nul = list(ptrs)
     nul[4] = None
     assert lib.kda_replay(*nul, -5.0, 4, 2, 9, 4, None) == NUL
+    # state on 16 bytes, records and tables on their element size (a call
+    # that passes every check would launch: not made with dummy pointers)
+    for i, addr, want in ((7, 0x1008, ALN), (0, 0x1002, ALN), (1, 0x1001, ALN), (4, 0x1002, ALN)):
+        mis = list(ptrs)
+        mis[i] = P(addr)
+        assert lib.kda_replay(*mis, -5.0, 4, 2, 9, 4, None) == want
 
 
 def test_binding_raises_value_error(lib):

@@ -201,6 +201,29 @@ def test_contract_errors_raise(gpu):
         gpu.run(d2)   # W < T + 2
 
 
+@pytest.mark.parametrize("name,shift", [("state", 1), ("f_a", 2), ("x", 1)])
+def test_misaligned_operand_raises(gpu, name, shift):
+    """A contiguous view that starts `shift` elements past an aligned address
+    (state: 4 bytes off 16; f_a: 4 bytes off 16; x: 2 bytes off 4) is refused
+    before any device work: the pools keep their bits."""
+    import torch
+
+    p = inputs.make_problem(dict(B=2, H=2, T=1, N=5, W=3, seed=5))
+    d = gpu.to_device(p)
+    t = d[name]
+    buf = torch.empty(t.numel() + shift, dtype=t.dtype, device=t.device)
+    mis = buf[shift:].view(t.shape)
+    mis.copy_(t)
+    state0, conv0 = d["state"].clone(), d["conv_state"].clone()
+    d2 = dict(d)
+    d2[name] = mis
+    with pytest.raises(ValueError, match="aligned"):
+        gpu.run(d2)
+    torch.cuda.synchronize()
+    assert torch.equal(d["state"], state0) and torch.equal(d["conv_state"], conv0)
+    assert torch.equal(mis, t)
+
+
 # --------------------------------------------------------------------------
 # the method's invariants, on the GPU
 
