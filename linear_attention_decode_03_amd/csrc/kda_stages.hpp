@@ -45,10 +45,14 @@ struct Inputs {
   float q[T][kD], k[T][kD], a[T][kD];
   float g[T][kD];  // FP32 gate projection before BF16 rounding
 };
+// Row pitch of the 16-row record tables: lanes (g, c) of an MFMA operand read
+// row c at column 4g, and P is stored at rows 4g + r, column c; with 132
+// floats per row both patterns fall in distinct banks.
+constexpr int kPad = kD + 4;
 template <int T>
 struct RecordOut {
-  float P[16][kD];  // S0 W
-  float C[16][16];  // W X^T
+  float P[16][kPad];  // S0 W
+  float C[16][16];    // W X^T
   float o[T][kD];
 };
 template <int T, bool kRecordBody>
@@ -66,10 +70,9 @@ struct Shared {
 
 // Record-mode operand tables: W rows A_t k_hat_t (t < T) and A_t q_hat_t
 // (T + t), X rows k_hat_t / A_t; rows beyond are zero.
-constexpr int kPad = kD + 4;  // W row pitch: the 16 rows read together fall in different banks
 struct RecordTables {
   float W[16][kPad];
-  float X[16][kD];
+  float X[16][kPad];
 };
 
 // ---- item resolution -----------------------------------------------------
