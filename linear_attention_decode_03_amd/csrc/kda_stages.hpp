@@ -83,29 +83,44 @@ struct Item {
   int dim;
 };
 
-// Slot resolution (uniform over the workgroup); false means padding.
+// The item of this workgroup (head-fastest numbering) and its token rows.
 template <int T>
-__device__ __forceinline__ bool resolve(const Args& A, Item& it) {
+__device__ __forceinline__ void locate(const Args& A, Item& it) {
   const int H = A.H;
   it.h = blockIdx.x % H;
   it.b = blockIdx.x / H;
   it.dim = H * kD;
   it.token0 = static_cast<size_t>(it.b) * T;
   it.off = 0;
+  it.rs = 0;
+  it.cs = 0;
+}
+
+// Slot resolution (uniform over the workgroup); false means padding.  Verify
+// reads the request's slot row (T entries, slot_stride >= T) together with
+// its accepted count, one round trip instead of two dependent ones, and
+// selects the read slot from the row.
+template <int T>
+__device__ __forceinline__ bool resolve(const Args& A, Item& it) {
   if constexpr (T == 1) {
     it.rs = A.slots[it.b];
     it.cs = it.rs;
     return it.rs > 0 && it.rs < A.N;
   } else {
     const int acc = A.accepted[it.b];
+    const int32_t* row = A.slots + static_cast<size_t>(it.b) * A.slot_stride;
+    int slot[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) slot[t] = row[t];
+    // One test of everything (no branch between the two loads and their use).
     const int lim = T < A.slot_stride ? T : A.slot_stride;
-    it.rs = 0;
-    it.cs = 0;
-    if (acc < 1 || acc > lim) return false;
     it.off = acc - 1;
-    it.rs = A.slots[static_cast<size_t>(it.b) * A.slot_stride + it.off];
-    it.cs = A.slots[static_cast<size_t>(it.b) * A.slot_stride];
-    return it.rs > 0 && it.rs < A.N && it.cs >= 0 && it.cs < A.N;
+    int rs = slot[0];
+#pragma unroll
+    for (int t = 1; t < T; ++t) rs = it.off == t ? slot[t] : rs;
+    it.rs = rs;
+    it.cs = slot[0];
+    return (acc >= 1) & (acc <= lim) & (rs > 0) & (rs < A.N) & (it.cs >= 0) & (it.cs < A.N);
   }
 }
 
@@ -208,12 +223,32 @@ __device__ __forceinline__ float tap_value(uint32_t bits) {
   return kConvF32 ? __uint_as_float(bits) : bf16_bits_to_f32(bits);
 }
 
-template <int T, bool kBias, bool kConvF32>
-__device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOperands<T>& co) {
+// Inputs, weights and bias: independent of the slot tables, so they are
+// issued before the slots are read.
+template <int T, bool kBias>
+__device__ __forceinline__ void conv_load_inputs(const Args& A, const Item& it,
+                                                 ConvOperands<T>& co) {
   const int wave = conv_wave();
   const int part = wave < 2 ? wave : 2;
   const size_t hc = static_cast<size_t>(it.h) * kD + 2 * (threadIdx.x & 63);
   const size_t ch = static_cast<size_t>(part) * it.dim + hc;
+#pragma unroll
+  for (int t = 0; t < T; ++t) co.x[t] = load_pair(A.x + (it.token0 + t) * 3 * it.dim + ch);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    co.w[i] = load_pair(A.conv_w + (static_cast<size_t>(part) * 4 + i) * it.dim + hc);
+  co.bias = kBias ? load_pair(A.conv_b + ch) : 0u;
+}
+
+// The three taps of the window (columns off .. off + 2) of the resolved
+// convolution slot.
+template <int T, bool kConvF32>
+__device__ __forceinline__ void conv_load_taps(const Args& A, const Item& it,
+                                               ConvOperands<T>& co) {
+  const int wave = conv_wave();
+  const int part = wave < 2 ? wave : 2;
+  const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD +
+                    2 * (threadIdx.x & 63);
   const size_t base = (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W + it.off;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -223,12 +258,6 @@ __device__ __forceinline__ void conv_load(const Args& A, const Item& it, ConvOpe
       co.tap[j][i] = kConvF32 ? static_cast<const uint32_t*>(A.conv_state)[at]
                               : static_cast<const uint16_t*>(A.conv_state)[at];
     }
-#pragma unroll
-  for (int t = 0; t < T; ++t) co.x[t] = load_pair(A.x + (it.token0 + t) * 3 * it.dim + ch);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    co.w[i] = load_pair(A.conv_w + (static_cast<size_t>(part) * 4 + i) * it.dim + hc);
-  co.bias = kBias ? load_pair(A.conv_b + ch) : 0u;
 }
 
 // The window is rewritten in place after it was read: [tap1, tap2, x_0 ..]

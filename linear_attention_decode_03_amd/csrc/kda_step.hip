@@ -44,21 +44,14 @@ namespace {
 template <int T, bool kRecord, bool kBias, bool kConvF32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void kda_step_kernel(const Args A) {
-  Item it;
-  if (!resolve<T>(A, it)) {  // padding: BF16 zeros, nothing else touched
-    write_padding<T>(A, it);
-    return;
-  }
-  __shared__ Shared<T, false> sh;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c16 = lane & 15;
-  const int row0 = 32 * (lane >> 4) + 8 * wave;
-  const int lane_off = (row0 * kD + 4 * c16) * 4;
-
   // 1. Input operands first, then the state page (one buffer resource per
   //    64 KiB page): the inputs are used while the page is still arriving.
+  //    The operands that do not depend on the slot tables are issued before
+  //    the tables are read.
+  Item it;
+  locate<T>(A, it);
   ConvOperands<T> co;
-  conv_load<T, kBias, kConvF32>(A, it, co);
+  conv_load_inputs<T, kBias>(A, it, co);
   GateOperands go;
   if constexpr (T == 1) gate_load(A, it, go);
   // Decode has no VGPRs to spare for these two; there they are loaded where
@@ -68,6 +61,17 @@ void kda_step_kernel(const Args A) {
     beta_logit = load_beta<T>(A, it);
     dt = load_dt(A, it);
   }
+  __builtin_amdgcn_sched_barrier(0);  // not sunk below the slot reads
+  if (!resolve<T>(A, it)) {  // padding: BF16 zeros, nothing else touched
+    write_padding<T>(A, it);
+    return;
+  }
+  __shared__ Shared<T, false> sh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15;
+  const int row0 = 32 * (lane >> 4) + 8 * wave;
+  const int lane_off = (row0 * kD + 4 * c16) * 4;
+  conv_load_taps<T, kConvF32>(A, it, co);
   OutputOperands<T> oo;
   float4 st[8][2];
   {
@@ -170,7 +174,22 @@ void kda_step_kernel(const Args A) {
 template <int T, bool kBias, bool kConvF32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void kda_record_kernel(const Args A) {
+  // 1. The input operands ahead of the state page (loads of a wave retire in
+  //    issue order, so nothing that the prologue needs may queue behind the
+  //    page): convolution inputs, gate rows, f_a, beta, dt_bias before the
+  //    slot tables are read, the window taps after; the output-norm operands
+  //    after the gate.  The scheduling barriers keep the groups in this order.
   Item it;
+  locate<T>(A, it);
+  ConvOperands<T> co;
+  conv_load_inputs<T, kBias>(A, it, co);
+  GateQuadOperands<T> go;
+  gate_quad_load_fb<T>(A, it, go, 0);
+  gate_quad_load_fb<T>(A, it, go, 1);
+  gate_quad_load_fa<T>(A, it, go);
+  const float beta_logit = load_beta<T>(A, it);
+  const float dt = load_dt(A, it);
+  __builtin_amdgcn_sched_barrier(0);
   if (!resolve<T>(A, it)) {
     write_padding<T>(A, it);
     return;
@@ -179,21 +198,7 @@ void kda_record_kernel(const Args A) {
   __shared__ RecordTables rt;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
-
-  // 1. The input operands ahead of the state page (loads of a wave retire in
-  //    issue order, so nothing that the prologue needs may queue behind the
-  //    page): convolution, gate rows, f_a, beta, dt_bias; the output-norm
-  //    operands after the gate.  The scheduling barriers keep the groups in
-  //    this order.
-  ConvOperands<T> co;
-  conv_load<T, kBias, kConvF32>(A, it, co);
-  __builtin_amdgcn_sched_barrier(0);
-  GateQuadOperands<T> go;
-  gate_quad_load_fb<T>(A, it, go, 0);
-  gate_quad_load_fb<T>(A, it, go, 1);
-  gate_quad_load_fa<T>(A, it, go);
-  const float beta_logit = load_beta<T>(A, it);
-  const float dt = load_dt(A, it);
+  conv_load_taps<T, kConvF32>(A, it, co);
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. Convolution, norms, gate projection.
