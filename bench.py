@@ -10,7 +10,8 @@ Prints one JSON line.  `value` is (request, head) items per second;
 `roofline` relates the kernel's algorithmic bytes per launch to its average
 duration, measured with HIP events around each launch on the launch stream
 (back-to-back launches); `roofline.cold` repeats that with a 1 GiB scratch
-write before each launch, so that no operand is cached;
+write before each launch, so that no operand is cached (and the caches hold
+dirty lines), `roofline.cold_clean` with a 1 GiB read instead;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
@@ -220,22 +221,30 @@ def main():
     print(f"[bench] {K} steps, {ms_per_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
-    # Cold launches: a 1 GiB scratch write before each one (outside the
-    # launch's own events) evicts the L2s and the memory-side cache.
+    # Cold launches: before each one (outside the launch's own events) a
+    # 1 GiB pass over a scratch buffer evicts the L2s and the memory-side
+    # cache.  "cold": the pass writes, so the caches are full of dirty lines
+    # that are written back while the launch runs; "clean": the pass only
+    # reads, so nothing of the launch is cached and nothing else is dirty.
     k_cold = max(0, args.cold_launches)
-    cold = []
+    cold, clean = [], []
     if k_cold:
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        cold_s = [torch.cuda.Event(enable_timing=True) for _ in range(k_cold)]
-        cold_e = [torch.cuda.Event(enable_timing=True) for _ in range(k_cold)]
-        for i in range(k_cold):
-            flush.fill_(float(i))
-            cold_s[i].record()
-            step()
-            cold_e[i].record()
-        torch.cuda.synchronize()
+        flush.fill_(1.0)
+        for mode, out_list in (("write", cold), ("read", clean)):
+            ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(k_cold)]
+            ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(k_cold)]
+            for i in range(k_cold):
+                if mode == "write":
+                    flush.fill_(float(i))
+                else:
+                    flush.sum()
+                ev_s[i].record()
+                step()
+                ev_e[i].record()
+            torch.cuda.synchronize()
+            out_list.extend(sorted(s_.elapsed_time(e_) for s_, e_ in zip(ev_s, ev_e)))
         del flush
-        cold = sorted(s_.elapsed_time(e_) for s_, e_ in zip(cold_s, cold_e))
 
     items = p["B"] * p["H"]
     abytes = replay_algorithmic_bytes(p) if replay else algorithmic_bytes(p)
@@ -270,7 +279,13 @@ def main():
                      "cold": None if not cold else {
                          "kernel_us_median": cold[k_cold // 2] * 1e3, "launches": k_cold,
                          "achieved": abytes / (cold[k_cold // 2] * 1e-3) / 1e9,
-                         "frac": abytes / (cold[k_cold // 2] * 1e-3) / 1e9 / HBM_PEAK_GBPS}},
+                         "frac": abytes / (cold[k_cold // 2] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "evicted_by": "1 GiB write (dirty lines written back during the launch)"},
+                     "cold_clean": None if not clean else {
+                         "kernel_us_median": clean[k_cold // 2] * 1e3, "launches": k_cold,
+                         "achieved": abytes / (clean[k_cold // 2] * 1e-3) / 1e9,
+                         "frac": abytes / (clean[k_cold // 2] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "evicted_by": "1 GiB read"}},
     }
     result["config"].update(extra)
     if not args.no_cpu:
