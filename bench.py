@@ -172,8 +172,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the KDA step has no cross-GPU exchange and "
-              "this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the KDA step has no cross-GPU exchange "
+              "(each GPU would run its own share of heads); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
