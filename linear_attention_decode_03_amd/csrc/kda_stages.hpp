@@ -83,6 +83,23 @@ struct Item {
   int dim;
 };
 
+// Verify: the request's slot row, slots[b, 0 .. T-1], read once.
+template <int T>
+struct SlotRow {
+  int s[T];
+};
+
+// Entry t of the slot row (t uniform): a chain of selects, so the row stays
+// in scalar registers (the readfirstlane keeps the compiler from turning the
+// chain into an indexed table in scratch memory).
+template <int T>
+__device__ __forceinline__ int row_slot(const SlotRow<T>& row, int t) {
+  int s = row.s[0];
+#pragma unroll
+  for (int u = 1; u < T; ++u) s = __builtin_amdgcn_readfirstlane(t == u ? row.s[u] : s);
+  return s;
+}
+
 // The item of this workgroup (head-fastest numbering) and its token rows.
 template <int T>
 __device__ __forceinline__ void locate(const Args& A, Item& it) {
@@ -101,7 +118,7 @@ __device__ __forceinline__ void locate(const Args& A, Item& it) {
 // its accepted count, one round trip instead of two dependent ones, and
 // selects the read slot from the row.
 template <int T>
-__device__ __forceinline__ bool resolve(const Args& A, Item& it) {
+__device__ __forceinline__ bool resolve(const Args& A, Item& it, SlotRow<T>& slot_row) {
   if constexpr (T == 1) {
     it.rs = A.slots[it.b];
     it.cs = it.rs;
@@ -109,17 +126,14 @@ __device__ __forceinline__ bool resolve(const Args& A, Item& it) {
   } else {
     const int acc = A.accepted[it.b];
     const int32_t* row = A.slots + static_cast<size_t>(it.b) * A.slot_stride;
-    int slot[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) slot[t] = row[t];
+    for (int t = 0; t < T; ++t) slot_row.s[t] = row[t];
     // One test of everything (no branch between the two loads and their use).
     const int lim = T < A.slot_stride ? T : A.slot_stride;
     it.off = acc - 1;
-    int rs = slot[0];
-#pragma unroll
-    for (int t = 1; t < T; ++t) rs = it.off == t ? slot[t] : rs;
+    const int rs = row_slot<T>(slot_row, it.off);
     it.rs = rs;
-    it.cs = slot[0];
+    it.cs = slot_row.s[0];
     return (acc >= 1) & (acc <= lim) & (rs > 0) & (rs < A.N) & (it.cs >= 0) & (it.cs < A.N);
   }
 }

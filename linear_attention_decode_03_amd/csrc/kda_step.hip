@@ -41,9 +41,16 @@ namespace {
 // 16-byte access of a wave covers four 256-byte row segments 16 KiB apart,
 // which spreads each instruction over more HBM channels; a row's keys sit in
 // one 16-lane DPP row.
-template <int T, bool kRecord, bool kBias, bool kConvF32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void kda_step_kernel(const Args A) {
+//
+// kLatency: the variant for batches small enough that every workgroup is
+// resident at 2 per CU (512 items).  There occupancy buys nothing and each
+// item's chain of memory round trips is the launch time, so the kernel takes
+// up to 256 VGPRs and issues every operand (beta, dt_bias, the output-norm
+// operands and, for T > 1, the whole gate operand set of the 4x4x4 FP64
+// projection) ahead of the state page: one round trip before the page
+// instead of one per gate step.
+template <int T, bool kRecord, bool kBias, bool kConvF32, bool kLatency>
+__device__ __forceinline__ void step_body(const Args& A) {
   // 1. Input operands first, then the state page (one buffer resource per
   //    64 KiB page): the inputs are used while the page is still arriving.
   //    The operands that do not depend on the slot tables are issued before
@@ -54,15 +61,24 @@ void kda_step_kernel(const Args A) {
   conv_load_inputs<T, kBias>(A, it, co);
   GateOperands go;
   if constexpr (T == 1) gate_load(A, it, go);
-  // Decode has no VGPRs to spare for these two; there they are loaded where
-  // they are used.
+  GateQuadOperands<T> gq;
+  if constexpr (T > 1 && kLatency) {
+    gate_quad_load_fb<T>(A, it, gq, 0);
+    gate_quad_load_fb<T>(A, it, gq, 1);
+    gate_quad_load_fa<T>(A, it, gq);
+  }
+  // Decode at full occupancy has no VGPRs to spare for these two; there they
+  // are loaded where they are used.
   float beta_logit = 0.0f, dt = 0.0f;
-  if constexpr (T > 1) {
+  if constexpr (T > 1 || kLatency) {
     beta_logit = load_beta<T>(A, it);
     dt = load_dt(A, it);
   }
+  OutputOperands<T> oo;
+  if constexpr (kLatency) load_output_operands<T>(A, it, oo);
   __builtin_amdgcn_sched_barrier(0);  // not sunk below the slot reads
-  if (!resolve<T>(A, it)) {  // padding: BF16 zeros, nothing else touched
+  SlotRow<T> slot_row;
+  if (!resolve<T>(A, it, slot_row)) {  // padding: BF16 zeros, nothing else touched
     write_padding<T>(A, it);
     return;
   }
@@ -72,7 +88,6 @@ void kda_step_kernel(const Args A) {
   const int row0 = 32 * (lane >> 4) + 8 * wave;
   const int lane_off = (row0 * kD + 4 * c16) * 4;
   conv_load_taps<T, kConvF32>(A, it, co);
-  OutputOperands<T> oo;
   float4 st[8][2];
   {
     const __amdgpu_buffer_rsrc_t page = page_rsrc(A.state, it.rs, it.h, A.H);
@@ -86,11 +101,16 @@ void kda_step_kernel(const Args A) {
 
   // 2. Inputs.
   conv_compute<T, kRecord, kConvF32>(A, it, sh, co);
-  if constexpr (T == 1) beta_logit = load_beta<T>(A, it);
+  if constexpr (T == 1 && !kLatency) beta_logit = load_beta<T>(A, it);
   store_beta<T>(sh, beta_logit);
-  if constexpr (T == 1) gate_valu(go, sh); else gate_mfma<T>(A, it, sh);
+  if constexpr (T == 1)
+    gate_valu(go, sh);
+  else if constexpr (kLatency)
+    gate_quad_compute<T>(gq, sh);
+  else
+    gate_mfma<T>(A, it, sh);
   __syncthreads();
-  if constexpr (T == 1) dt = load_dt(A, it);
+  if constexpr (T == 1 && !kLatency) dt = load_dt(A, it);
   decay<T, kRecord>(A, it, sh, dt);
   __syncthreads();
 
@@ -138,7 +158,7 @@ void kda_step_kernel(const Args A) {
       }
     }
     if constexpr (!kRecord) {
-      const int target = T == 1 ? it.rs : A.slots[static_cast<size_t>(it.b) * A.slot_stride + t];
+      const int target = T == 1 ? it.rs : row_slot<T>(slot_row, t);
       if (target > 0 && target < A.N) {
         float* page = page_ptr(A.state, target, it.h, A.H);
 #pragma unroll
@@ -148,12 +168,24 @@ void kda_step_kernel(const Args A) {
       }
     }
   }
-  load_output_operands<T>(A, it, oo);
+  if constexpr (!kLatency) load_output_operands<T>(A, it, oo);
   __syncthreads();
 
   // 4. Gated RMSNorm.
   gated_rmsnorm<T>(A, it, sh, sh.o, oo);
   keep_alive(A, sink);
+}
+
+template <int T, bool kRecord, bool kBias, bool kConvF32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void kda_step_kernel(const Args A) {
+  step_body<T, kRecord, kBias, kConvF32, false>(A);
+}
+
+template <int T, bool kRecord, bool kBias, bool kConvF32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void kda_step_latency_kernel(const Args A) {
+  step_body<T, kRecord, kBias, kConvF32, true>(A);
 }
 
 // ---- record mode (RecoverSSM verify): all tokens from one pass over S0 -------
@@ -190,7 +222,8 @@ void kda_record_kernel(const Args A) {
   const float beta_logit = load_beta<T>(A, it);
   const float dt = load_dt(A, it);
   __builtin_amdgcn_sched_barrier(0);
-  if (!resolve<T>(A, it)) {
+  SlotRow<T> slot_row;
+  if (!resolve<T>(A, it, slot_row)) {
     write_padding<T>(A, it);
     return;
   }
@@ -346,6 +379,10 @@ kda_status check(const Args& A, int T, int record, int gate_mode) {
   return KDA_OK;
 }
 
+// Up to this many items every workgroup of the latency variant is resident
+// at once (2 per CU on 256 CUs).
+constexpr long long kLatencyItems = 512;
+
 // Record mode takes the closed-form kernel when the running decay products
 // stay normal FP32 numbers (|lower_bound| <= 10, at most 8 tokens: |log A_t| <= 80).
 constexpr float kRecordBound = 10.0f;
@@ -360,7 +397,11 @@ kda_status launch_v(const Args& A, hipStream_t stream) {
       return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
     }
   }
-  hipLaunchKernelGGL((kda_step_kernel<T, kRecord, kBias, kConvF32>), grid, block, 0, stream, A);
+  if (static_cast<long long>(A.B) * A.H <= kLatencyItems)
+    hipLaunchKernelGGL((kda_step_latency_kernel<T, kRecord, kBias, kConvF32>), grid, block, 0,
+                       stream, A);
+  else
+    hipLaunchKernelGGL((kda_step_kernel<T, kRecord, kBias, kConvF32>), grid, block, 0, stream, A);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

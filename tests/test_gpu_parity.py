@@ -579,3 +579,62 @@ def test_random_small_configs(gpu, k):
             if p["B"] > 2:       # and a skipped write target elsewhere
                 p["slots"][(b + 1) % p["B"], p["T"] - 1] = 0
     check(gpu, p, f"random {k}: {cfg} bias={bias} pad={pad}")
+
+
+# --------------------------------------------------------------------------
+# the two launch shapes of the step: up to 512 items every workgroup is
+# resident at 2 per CU and the latency kernel runs (all operands ahead of the
+# page); above, the full-occupancy kernel
+
+
+def _request_slice(d, lo, hi):
+    """The device operands of requests lo .. hi-1 (views; pools and weights shared)."""
+    T = d["T"]
+    out = dict(d)
+    for k in ("x", "f_a", "beta", "gate", "out"):
+        out[k] = d[k][lo * T:hi * T]
+    for k in ("slots", "accepted", "rec_u", "rec_kg"):
+        if d.get(k) is not None:
+            out[k] = d[k][lo:hi]
+    return out
+
+
+@pytest.mark.parametrize("T,record,conv_f32", [(1, 0, 0), (2, 0, 0), (3, 0, 1), (5, 0, 0),
+                                               (6, 0, 0), (7, 0, 1), (8, 0, 0), (8, 1, 0)])
+def test_full_occupancy_kernel_and_latency_kernel(gpu, T, record, conv_f32):
+    """B*H = 640 items: the full-occupancy kernel against the oracle, then the
+    same requests as two calls of 320 items each (the latency kernel) must
+    leave every pool, output and record bit for bit as the single call did
+    (the gate projection is exact in both, every other operation the same).
+    record with lower_bound -12 takes the token-by-token record path."""
+    import torch
+
+    cfg = dict(B=40, H=16, T=T, W=3 if T == 1 else T + 2, seed=4100 + T, record=record,
+               conv_f32=conv_f32)
+    if T > 1:
+        cfg.update(slot_stride=T, N=40 * T + 3)
+    else:
+        cfg.update(N=43)
+    if record:
+        cfg["lower_bound"] = -12.0
+    p = inputs.make_problem(cfg)
+    if T > 1:
+        p["accepted"][3] = 0      # a padded request in each half
+        p["accepted"][27] = 0
+    else:
+        p["slots"][3] = 0
+        p["slots"][27] = 0
+    check(gpu, p, f"full occupancy T={T} record={record} conv_f32={conv_f32}")
+
+    one = gpu.to_device(p)
+    gpu.run(one)
+    two = gpu.to_device(p)
+    gpu.run(_request_slice(two, 0, 20))
+    gpu.run(_request_slice(two, 20, 40))
+    torch.cuda.synchronize()
+    a, b = gpu.to_host(one), gpu.to_host(two)
+    for k in ("state", "conv_state", "out", "rec_u", "rec_kg"):
+        if a[k] is None:
+            continue
+        va, vb = a[k].view(np.uint8), b[k].view(np.uint8)
+        assert np.array_equal(va, vb), f"{k}: the latency kernel differs from the full-occupancy kernel"
