@@ -599,24 +599,24 @@ def _request_slice(d, lo, hi):
     return out
 
 
-@pytest.mark.parametrize("T,record,conv_f32", [(1, 0, 0), (2, 0, 0), (3, 0, 1), (5, 0, 0),
-                                               (6, 0, 0), (7, 0, 1), (8, 0, 0), (8, 1, 0)])
-def test_full_occupancy_kernel_and_latency_kernel(gpu, T, record, conv_f32):
+@pytest.mark.parametrize("T,record,conv_f32,lower_bound", [
+    (1, 0, 0, -5.0), (2, 0, 0, -5.0), (3, 0, 1, -5.0), (5, 0, 0, -5.0), (6, 0, 0, -5.0),
+    (7, 0, 1, -5.0), (8, 0, 0, -5.0), (8, 1, 0, -12.0), (4, 1, 0, -5.0), (8, 1, 1, -5.0)])
+def test_full_occupancy_kernel_and_latency_kernel(gpu, T, record, conv_f32, lower_bound):
     """B*H = 640 items: the full-occupancy kernel against the oracle, then the
     same requests as two calls of 320 items each (the latency kernel) must
     leave every pool, output and record bit for bit as the single call did
     (the gate projection is exact in both, every other operation the same).
-    record with lower_bound -12 takes the token-by-token record path."""
+    Record mode with lower_bound -12 takes the token-by-token path, with -5
+    the closed-form record kernel."""
     import torch
 
-    cfg = dict(B=40, H=16, T=T, W=3 if T == 1 else T + 2, seed=4100 + T, record=record,
-               conv_f32=conv_f32)
+    cfg = dict(B=40, H=16, T=T, W=3 if T == 1 else T + 2, seed=4100 + 10 * record + T,
+               record=record, conv_f32=conv_f32, lower_bound=lower_bound)
     if T > 1:
         cfg.update(slot_stride=T, N=40 * T + 3)
     else:
         cfg.update(N=43)
-    if record:
-        cfg["lower_bound"] = -12.0
     p = inputs.make_problem(cfg)
     if T > 1:
         p["accepted"][3] = 0      # a padded request in each half
@@ -624,7 +624,7 @@ def test_full_occupancy_kernel_and_latency_kernel(gpu, T, record, conv_f32):
     else:
         p["slots"][3] = 0
         p["slots"][27] = 0
-    check(gpu, p, f"full occupancy T={T} record={record} conv_f32={conv_f32}")
+    check(gpu, p, f"full occupancy T={T} record={record} conv_f32={conv_f32} lb={lower_bound}")
 
     one = gpu.to_device(p)
     gpu.run(one)
