@@ -134,9 +134,56 @@ def cpu_baseline(p, replay=False, min_seconds=10.0):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    return {"value": done / el, "unit": "items/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done // n_items} full pass(es) over the {n_items} items of the "
-                      f"same workload, single-threaded, {el:.1f} s"}
+    res = {"value": done / el, "unit": "items/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done // n_items} full pass(es) over the {n_items} items of the "
+                     f"same workload, single-threaded, {el:.1f} s",
+           "cpu_model": cpu_model()}
+    if not replay:
+        res["threaded"] = cpu_baseline_threaded(q, min_seconds=min_seconds / 2)
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_threaded(q, min_seconds=5.0, max_threads=16):
+    """The same oracle on the same problem with its items split statically
+    over host threads: one contiguous block of item ids per thread, each a
+    plain oracle call on that block (the C code holds an item's state on its
+    own stack and items touch disjoint memory; ctypes releases the GIL for
+    the call).  Threads: the cores this process may run on, at most
+    `max_threads`."""
+    import threading
+
+    import numpy as np
+
+    import oracle
+
+    n_items = q["B"] * q["H"]
+    n = max(1, min(max_threads, len(os.sched_getaffinity(0)), n_items))
+    blocks = np.array_split(np.arange(n_items, dtype=np.int32), n)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        ts = [threading.Thread(target=oracle.run, args=(q,), kwargs={"items": blk})
+              for blk in blocks]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        done += n_items
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": done / el, "unit": "items/s", "cores": n,
+            "sample": f"{done // n_items} full pass(es) over the {n_items} items, "
+                      f"static split over {n} threads, {el:.1f} s"}
 
 
 def run_copy(args):
