@@ -8,10 +8,12 @@ seeded synthetic inputs resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is (request, head) items per second;
 `roofline` relates the kernel's algorithmic bytes per launch to its average
-duration, measured with HIP events around each launch on the launch stream
-(back-to-back launches); `roofline.cold` repeats that with a 1 GiB scratch
-write before each launch, so that no operand is cached (and the caches hold
-dirty lines), `roofline.cold_clean` with a 1 GiB read instead;
+duration: the span of one pair of HIP events on the launch stream around the
+K back-to-back launches of the timed region, divided by K
+(`single_launch_us` gives the spread of launches timed one by one in a
+second pass); `roofline.cold` times launches each preceded by a 1 GiB
+scratch write, so that no operand is cached (and the caches hold dirty
+lines), `roofline.cold_clean` with a 1 GiB read instead;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
@@ -251,22 +253,36 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # The timed region: exactly K back-to-back steps between one pair of
+    # events on the launch stream (nothing else is enqueued between the
+    # launches), bracketed by device synchronisations.  The events' span / K
+    # is the average launch duration, gaps between launches included.
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(K):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    kernel_ms = ev0.elapsed_time(ev1) / K
+    print(f"[bench] {K} steps, {ms_per_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    # Spread of single launches: a second pass (outside the timed region)
+    # with an event pair around every launch.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     for i in range(K):
         starts[i].record()
         step()
         ends[i].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    durations_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_per_step = wall * 1e3 / K
-    kernel_ms = sum(durations_ms) / K
-    print(f"[bench] {K} steps, {ms_per_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
+    single = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
 
     # Cold launches: before each one (outside the launch's own events) a
     # 1 GiB pass over a scratch buffer evicts the L2s and the memory-side
@@ -323,6 +339,9 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": abytes,
                      "kernel_us": kernel_ms * 1e3,
+                     "single_launch_us": {"p10": single[K // 10] * 1e3,
+                                          "median": single[K // 2] * 1e3,
+                                          "p90": single[(9 * K) // 10] * 1e3},
                      "cold": None if not cold else {
                          "kernel_us_median": cold[k_cold // 2] * 1e3, "launches": k_cold,
                          "achieved": abytes / (cold[k_cold // 2] * 1e-3) / 1e9,
