@@ -37,6 +37,14 @@ def load_library(path: str = LIB_PATH):
     if _lib is None:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        # torch carries its own HIP runtime (soname libamdhip64.so.7, loaded
+        # by torch under the name libamdhip64.so).  It has to be in the
+        # process before the library, whose libamdhip64.so.7 dependency then
+        # binds to it; loaded the other way round the process holds two HIP
+        # runtimes, and torch's streams and allocations are not the
+        # library's (launches on a torch stream fail).
+        import torch  # noqa: F401
+
         lib = ctypes.CDLL(path)
         lib.kda_decode.restype = _I
         lib.kda_decode.argtypes = _OPERANDS + [_I] * 6 + [_P]

@@ -178,3 +178,32 @@ def test_binding_refuses_host_tensors():
                        torch.from_numpy(r["a_log"]), torch.from_numpy(r["dt_bias"]),
                        torch.from_numpy(r["src"]), torch.from_numpy(r["dst"]),
                        torch.from_numpy(r["n"]), torch.from_numpy(r["state"]), -5.0)
+
+
+_ONE_RUNTIME = r"""
+import sys
+sys.path.insert(0, {root!r})
+from linear_attention_decode_03_amd import kda
+kda.load_library()          # before the caller has imported torch
+import torch                # noqa: F401
+paths = set()
+for line in open("/proc/self/maps"):
+    f = line.split()[-1]
+    if "libamdhip64" in f:
+        paths.add(f)
+print(len(paths), sorted(paths))
+"""
+
+
+def test_library_loaded_first_shares_torch_hip_runtime():
+    # torch carries its own HIP runtime; the library must bind to that one
+    # even when it is loaded before the caller imports torch, or the process
+    # holds two runtimes and torch's streams are invalid in the library's.
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, "-c", _ONE_RUNTIME.format(root=ROOT)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    n = int(r.stdout.split()[0])
+    assert n == 1, r.stdout
