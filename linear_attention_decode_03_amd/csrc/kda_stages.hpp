@@ -391,53 +391,9 @@ __device__ __forceinline__ void gate_valu(const GateOperands& go, SH& sh) {
   }
 }
 
-// Several tokens: FP64 MFMA 16x16x4, D[feature][token] over K = 128 columns
-// (tokens >= T are zero columns).  Wave w computes feature tiles 32w and
-// 32w + 16.  Lane (g = l >> 4, c = l & 15) feeds A[c][g] = F_B[f0 + c][k] and
-// B[g][c] = f_a[token c][k] with k = 32q + 8g + e at step (q, e): each lane's
-// operands are 16-byte loads; the 128 columns are visited in that order.  D layout of this instruction: lane l,
-// element r holds D[l/16 + 4r][l%16].
-template <int T, class SH>
-__device__ __forceinline__ void gate_mfma(const Args& A, const Item& it, SH& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-#pragma unroll 1
-  for (int tile = 0; tile < 2; ++tile) {
-    const int f0 = 32 * wave + 16 * tile;
-    // Two independent accumulation chains (even and odd 32-column quarters);
-    // the sums are exact in FP64, so the chain structure does not change a bit.
-    f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
-#pragma unroll 1
-    for (int q0 = 0; q0 < 4; q0 += 2) {
-      uint4 fb[2], fa[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q = q0 + j;
-        fb[j] = *reinterpret_cast<const uint4*>(
-            A.f_b + (static_cast<size_t>(it.h) * kD + f0 + c) * kD + 32 * q + 8 * g);
-        fa[j] = make_uint4(0, 0, 0, 0);
-        if (c < T)
-          fa[j] = *reinterpret_cast<const uint4*>(A.f_a + (it.token0 + c) * kD + 32 * q + 8 * g);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(bf16_at(fb[j], e)),
-                                                         static_cast<double>(bf16_at(fa[j], e)),
-                                                         acc[j], 0, 0, 0);
-    }
-    if (c < T) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sh.u.in.g[c][f0 + g + 4 * r] = static_cast<float>(acc[0][r] + acc[1][r]);
-    }
-  }
-}
-
-// The same product on FP64 MFMA 4x4x4 (four 4x4 blocks per instruction, 16
-// cycles against 64 for 16x16x4): no padding columns when T is not a
-// multiple of 16, so half the cycles at T = 8 and a quarter at T <= 4.
+// Several tokens: the gate projection on FP64 MFMA 4x4x4 (four 4x4 blocks
+// per instruction, 16 cycles; a 16x16x4 tile takes 64 and has 16 token
+// columns, so this needs half its cycles at T = 8 and a quarter at T <= 4).
 // Lane layout of the instruction: block b = (l >> 2) & 3; A: lane
 // 16k + 4b + i holds A[i][k]; B: lane 16k + 4b + j holds B[k][j]; D: lane
 // 16i + 4b + j holds D[i][j].  Block b = feature quad: A[i][k] =
@@ -511,6 +467,79 @@ __device__ __forceinline__ void gate_quad_compute(const GateQuadOperands<T>& go,
 #pragma unroll
   for (int fg = 0; fg < 2; ++fg) {
     const int f = 32 * wave + 16 * fg + 4 * b + i;
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg) {
+      const int t = 4 * tg + j;
+      if (t < T) sh.u.in.g[t][f] = static_cast<float>(acc[fg][tg]);
+    }
+  }
+}
+
+// The same 4x4x4 product for a kernel that holds the state page in its
+// registers meanwhile: the operands of column step n (8 columns of each
+// 32-column quarter) arrive in a round of their own, and the round for step
+// n + 1 is requested before step n is computed, so two rounds are live at
+// most (2 x (2 + kTG) 16-byte loads) instead of the whole set.  The last
+// step requests its own columns again (cache hits, unused) so that no load
+// sits under a branch.
+template <int T, class SH>
+__device__ __forceinline__ void gate_quad_rounds(const Args& A, const Item& it, SH& sh) {
+  constexpr int kTG = GateQuadOperands<T>::kTokenGroups;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int k = lane >> 4, b = (lane >> 2) & 3, i = lane & 3, j = lane & 3;
+  // Wave-uniform bases, 32-bit lane offsets (in elements); the second
+  // feature group sits 16 rows below the first.
+  const uint16_t* fb_base = A.f_b + static_cast<size_t>(it.h) * kD * kD;
+  const uint16_t* fa_base = A.f_a + it.token0 * kD;
+  const uint32_t fb_off = (32 * wave + 4 * b + i) * kD + 32 * k;
+  uint32_t fa_off[kTG];
+#pragma unroll
+  for (int tg = 0; tg < kTG; ++tg) {
+    const int tok = 4 * tg + j < T ? 4 * tg + j : T - 1;
+    fa_off[tg] = tok * kD + 32 * k;
+  }
+  uint4 fb[2], fa[kTG];
+#pragma unroll
+  for (int fg = 0; fg < 2; ++fg)
+    fb[fg] = *reinterpret_cast<const uint4*>(fb_base + fb_off + 16 * kD * fg);
+#pragma unroll
+  for (int tg = 0; tg < kTG; ++tg) fa[tg] = *reinterpret_cast<const uint4*>(fa_base + fa_off[tg]);
+  double acc[2][kTG];
+#pragma unroll
+  for (int fg = 0; fg < 2; ++fg)
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg) acc[fg][tg] = 0.0;
+#pragma unroll 1
+  for (int n = 0; n < 4; ++n) {
+    const uint32_t col = 8 * (n < 3 ? n + 1 : n);
+    uint4 fb_next[2], fa_next[kTG];
+#pragma unroll
+    for (int fg = 0; fg < 2; ++fg)
+      fb_next[fg] = *reinterpret_cast<const uint4*>(fb_base + fb_off + 16 * kD * fg + col);
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg)
+      fa_next[tg] = *reinterpret_cast<const uint4*>(fa_base + fa_off[tg] + col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double bv[kTG];
+#pragma unroll
+      for (int tg = 0; tg < kTG; ++tg) bv[tg] = static_cast<double>(bf16_at(fa[tg], e));
+#pragma unroll
+      for (int fg = 0; fg < 2; ++fg) {
+        const double av = static_cast<double>(bf16_at(fb[fg], e));
+#pragma unroll
+        for (int tg = 0; tg < kTG; ++tg)
+          acc[fg][tg] = __builtin_amdgcn_mfma_f64_4x4x4f64(av, bv[tg], acc[fg][tg], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int fg = 0; fg < 2; ++fg) fb[fg] = fb_next[fg];
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg) fa[tg] = fa_next[tg];
+  }
+#pragma unroll
+  for (int fg = 0; fg < 2; ++fg) {
+    const int f = 32 * wave + 16 * fg + 4 * b + (lane >> 4);
 #pragma unroll
     for (int tg = 0; tg < kTG; ++tg) {
       const int t = 4 * tg + j;

@@ -108,7 +108,7 @@ __device__ __forceinline__ void step_body(const Args& A) {
   else if constexpr (kLatency)
     gate_quad_compute<T>(gq, sh);
   else
-    gate_mfma<T>(A, it, sh);
+    gate_quad_rounds<T>(A, it, sh);
   __syncthreads();
   if constexpr (T == 1 && !kLatency) dt = load_dt(A, it);
   decay<T, kRecord>(A, it, sh, dt);

@@ -400,6 +400,51 @@ def test_nondefault_stream(gpu):
     _parity.compare_step(before, ref, gpu.to_host(d), taps)
 
 
+_LOAD_FIRST = r"""
+import sys
+sys.path.insert(0, {root!r})
+from linear_attention_decode_03_amd import kda
+kda.load_library()          # before the caller has imported torch
+import numpy as np
+import torch
+from linear_attention_decode_03_amd import inputs
+from tests import _gpu
+p = inputs.make_problem(dict(B=3, H=4, T=4, N=13, W=6, seed=1003))
+d = _gpu.to_device(p)
+s = torch.cuda.Stream()
+torch.cuda.synchronize()
+with torch.cuda.stream(s):
+    _gpu.run(d, stream=s)
+s.synchronize()
+h = _gpu.to_host(d)
+np.savez({out!r}, **{{k: v for k, v in h.items() if v is not None}})
+print("done", flush=True)
+"""
+
+
+def test_library_loaded_before_torch(gpu, tmp_path):
+    # A fresh process that loads the library before importing torch, then
+    # launches a verify step on a torch stream: the library must share
+    # torch's HIP runtime (one runtime in the process), so the launch runs.
+    import os
+    import subprocess
+
+    out = str(tmp_path / "load_first.npz")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("[load-first] subprocess: library loaded before torch, verify T=4 on a torch stream")
+    r = subprocess.run([sys.executable, "-c", _LOAD_FIRST.format(root=root, out=out)],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-1000:] + r.stderr[-2000:]
+    p = inputs.make_problem(dict(B=3, H=4, T=4, N=13, W=6, seed=1003))
+    before = copy_problem(p)
+    ref = copy_problem(p)
+    taps = oracle.run(ref, taps=True)
+    got = dict(np.load(out))
+    for k in ("rec_u", "rec_kg"):
+        got.setdefault(k, None)
+    _parity.compare_step(before, ref, got, taps)
+
+
 # --------------------------------------------------------------------------
 # HIP graph capture: a decode and a verify step recorded once, replayed
 
