@@ -38,17 +38,18 @@ struct Args {
 
 // ---- shared memory -----------------------------------------------------------
 
+// Row pitch of the record tables: lanes (g, c) of an MFMA operand read row c
+// at column 4g, and P is stored at rows 4g + r, column c; with 132 floats
+// per row both patterns fall in distinct banks.
+constexpr int kPad = kD + 4;
 // Per-item tables.  q, k, a and g are dead once the inputs are reduced to
-// what the body needs; the record-mode body reuses their space for P, C and o.
+// what the body needs; the record-mode body reuses their space for P, C and
+// o, and the space of g (dead after the decay) for its X table.
 template <int T>
 struct Inputs {
   float q[T][kD], k[T][kD], a[T][kD];
-  float g[T][kD];  // FP32 gate projection before BF16 rounding
+  float g[T][kPad];  // FP32 gate projection before BF16 rounding
 };
-// Row pitch of the 16-row record tables: lanes (g, c) of an MFMA operand read
-// row c at column 4g, and P is stored at rows 4g + r, column c; with 132
-// floats per row both patterns fall in distinct banks.
-constexpr int kPad = kD + 4;
 template <int T>
 struct RecordOut {
   float P[16][kPad];  // S0 W
@@ -68,11 +69,11 @@ struct Shared {
   float os[T][2];     // [token][wave 0, 1]
 };
 
-// Record-mode operand tables: W rows A_t k_hat_t (t < T) and A_t q_hat_t
-// (T + t), X rows k_hat_t / A_t; rows beyond are zero.
+// Record-mode operand table W: rows A_t k_hat_t (t < T) and A_t q_hat_t
+// (T + t); rows beyond are zero.  (Its X rows, k_hat_t / A_t, live in the
+// space of Inputs::g.)
 struct RecordTables {
   float W[16][kPad];
-  float X[16][kPad];
 };
 
 // ---- item resolution -----------------------------------------------------
@@ -475,35 +476,51 @@ __device__ __forceinline__ void gate_quad_compute(const GateQuadOperands<T>& go,
   }
 }
 
-// The same 4x4x4 product for a kernel that holds the state page in its
-// registers meanwhile: the operands of column step n (8 columns of each
-// 32-column quarter) arrive in a round of their own, and the round for step
-// n + 1 is requested before step n is computed, so two rounds are live at
-// most (2 x (2 + kTG) 16-byte loads) instead of the whole set.  The last
-// step requests its own columns again (cache hits, unused) so that no load
-// sits under a branch.
-template <int T, class SH>
-__device__ __forceinline__ void gate_quad_rounds(const Args& A, const Item& it, SH& sh) {
-  constexpr int kTG = GateQuadOperands<T>::kTokenGroups;
+// The same 4x4x4 product with its operands in rounds, for kernels that
+// cannot hold the whole set: the operands of column step n (8 columns of
+// each 32-column quarter) arrive in a round of their own, and the round for
+// step n + 1 is requested before step n is computed, so at most two rounds
+// are live (2 x (2 + kTG) 16-byte loads).  gate_rounds_begin issues round 0
+// (early, where the kernel has registers to spare); gate_rounds_compute
+// runs the four steps.  The last step requests its own columns again (cache
+// hits, unused) so that no load sits under a branch.
+template <int T>
+struct GateRounds {
+  static constexpr int kTG = GateQuadOperands<T>::kTokenGroups;
+  const uint16_t* fb_base;  // wave-uniform bases ...
+  const uint16_t* fa_base;
+  uint32_t fb_off;          // ... and lane offsets in elements
+  uint32_t fa_off[kTG];
+  uint4 fb[2], fa[kTG];     // the current round
+};
+
+template <int T>
+__device__ __forceinline__ void gate_rounds_begin(const Args& A, const Item& it,
+                                                  GateRounds<T>& gr) {
+  constexpr int kTG = GateRounds<T>::kTG;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int k = lane >> 4, b = (lane >> 2) & 3, i = lane & 3, j = lane & 3;
-  // Wave-uniform bases, 32-bit lane offsets (in elements); the second
-  // feature group sits 16 rows below the first.
-  const uint16_t* fb_base = A.f_b + static_cast<size_t>(it.h) * kD * kD;
-  const uint16_t* fa_base = A.f_a + it.token0 * kD;
-  const uint32_t fb_off = (32 * wave + 4 * b + i) * kD + 32 * k;
-  uint32_t fa_off[kTG];
+  gr.fb_base = A.f_b + static_cast<size_t>(it.h) * kD * kD;
+  gr.fa_base = A.f_a + it.token0 * kD;
+  gr.fb_off = (32 * wave + 4 * b + i) * kD + 32 * k;  // feature group 1: 16 rows on
 #pragma unroll
   for (int tg = 0; tg < kTG; ++tg) {
     const int tok = 4 * tg + j < T ? 4 * tg + j : T - 1;
-    fa_off[tg] = tok * kD + 32 * k;
+    gr.fa_off[tg] = tok * kD + 32 * k;
   }
-  uint4 fb[2], fa[kTG];
 #pragma unroll
   for (int fg = 0; fg < 2; ++fg)
-    fb[fg] = *reinterpret_cast<const uint4*>(fb_base + fb_off + 16 * kD * fg);
+    gr.fb[fg] = *reinterpret_cast<const uint4*>(gr.fb_base + gr.fb_off + 16 * kD * fg);
 #pragma unroll
-  for (int tg = 0; tg < kTG; ++tg) fa[tg] = *reinterpret_cast<const uint4*>(fa_base + fa_off[tg]);
+  for (int tg = 0; tg < kTG; ++tg)
+    gr.fa[tg] = *reinterpret_cast<const uint4*>(gr.fa_base + gr.fa_off[tg]);
+}
+
+template <int T, class SH>
+__device__ __forceinline__ void gate_rounds_compute(GateRounds<T>& gr, SH& sh) {
+  constexpr int kTG = GateRounds<T>::kTG;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = (lane >> 2) & 3, j = lane & 3;
   double acc[2][kTG];
 #pragma unroll
   for (int fg = 0; fg < 2; ++fg)
@@ -515,27 +532,27 @@ __device__ __forceinline__ void gate_quad_rounds(const Args& A, const Item& it, 
     uint4 fb_next[2], fa_next[kTG];
 #pragma unroll
     for (int fg = 0; fg < 2; ++fg)
-      fb_next[fg] = *reinterpret_cast<const uint4*>(fb_base + fb_off + 16 * kD * fg + col);
+      fb_next[fg] = *reinterpret_cast<const uint4*>(gr.fb_base + gr.fb_off + 16 * kD * fg + col);
 #pragma unroll
     for (int tg = 0; tg < kTG; ++tg)
-      fa_next[tg] = *reinterpret_cast<const uint4*>(fa_base + fa_off[tg] + col);
+      fa_next[tg] = *reinterpret_cast<const uint4*>(gr.fa_base + gr.fa_off[tg] + col);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       double bv[kTG];
 #pragma unroll
-      for (int tg = 0; tg < kTG; ++tg) bv[tg] = static_cast<double>(bf16_at(fa[tg], e));
+      for (int tg = 0; tg < kTG; ++tg) bv[tg] = static_cast<double>(bf16_at(gr.fa[tg], e));
 #pragma unroll
       for (int fg = 0; fg < 2; ++fg) {
-        const double av = static_cast<double>(bf16_at(fb[fg], e));
+        const double av = static_cast<double>(bf16_at(gr.fb[fg], e));
 #pragma unroll
         for (int tg = 0; tg < kTG; ++tg)
           acc[fg][tg] = __builtin_amdgcn_mfma_f64_4x4x4f64(av, bv[tg], acc[fg][tg], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int fg = 0; fg < 2; ++fg) fb[fg] = fb_next[fg];
+    for (int fg = 0; fg < 2; ++fg) gr.fb[fg] = fb_next[fg];
 #pragma unroll
-    for (int tg = 0; tg < kTG; ++tg) fa[tg] = fa_next[tg];
+    for (int tg = 0; tg < kTG; ++tg) gr.fa[tg] = fa_next[tg];
   }
 #pragma unroll
   for (int fg = 0; fg < 2; ++fg) {

@@ -107,8 +107,11 @@ __device__ __forceinline__ void step_body(const Args& A) {
     gate_valu(go, sh);
   else if constexpr (kLatency)
     gate_quad_compute<T>(gq, sh);
-  else
-    gate_quad_rounds<T>(A, it, sh);
+  else {
+    GateRounds<T> gr;
+    gate_rounds_begin<T>(A, it, gr);
+    gate_rounds_compute<T>(gr, sh);
+  }
   __syncthreads();
   if constexpr (T == 1 && !kLatency) dt = load_dt(A, it);
   decay<T, kRecord>(A, it, sh, dt);
@@ -204,7 +207,7 @@ void kda_step_latency_kernel(const Args A) {
 // 16q + 4g + [0, 4)).  Used when |lower_bound| <= 10, so that every A_t and
 // 1 / A_t stays a normal FP32 number (|log A_t| <= 80).
 template <int T, bool kBias, bool kConvF32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void kda_record_kernel(const Args A) {
   // 1. The input operands ahead of the state page (loads of a wave retire in
   //    issue order, so nothing that the prologue needs may queue behind the
@@ -215,10 +218,8 @@ void kda_record_kernel(const Args A) {
   locate<T>(A, it);
   ConvOperands<T> co;
   conv_load_inputs<T, kBias>(A, it, co);
-  GateQuadOperands<T> go;
-  gate_quad_load_fb<T>(A, it, go, 0);
-  gate_quad_load_fb<T>(A, it, go, 1);
-  gate_quad_load_fa<T>(A, it, go);
+  GateRounds<T> gr;
+  gate_rounds_begin<T>(A, it, gr);
   const float beta_logit = load_beta<T>(A, it);
   const float dt = load_dt(A, it);
   __builtin_amdgcn_sched_barrier(0);
@@ -237,7 +238,7 @@ void kda_record_kernel(const Args A) {
   // 2. Convolution, norms, gate projection.
   conv_compute<T, true, kConvF32>(A, it, sh, co);
   store_beta<T>(sh, beta_logit);
-  gate_quad_compute<T>(go, sh);
+  gate_rounds_compute<T>(gr, sh);
   OutputOperands<T> oo;
   load_output_operands<T>(A, it, oo);
   __syncthreads();
@@ -260,7 +261,9 @@ void kda_record_kernel(const Args A) {
   decay<T, true>(A, it, sh, dt);
   __syncthreads();
 
-  // 4. W and X (thread = key channel), zero rows beyond 2T and T.
+  // 4. W and X (thread = key channel), W zero beyond row 2T.  X takes the
+  //    space of the FP32 gate projection, dead since the decay.
+  float (&X)[T][kPad] = sh.u.in.g;
   if (tid < kD) {
     const int key = tid;
     float acc = 1.0f;
@@ -273,20 +276,20 @@ void kda_record_kernel(const Args A) {
       const float qh = (sh.u.in.q[t][key] * fq) * A.scale;
       rt.W[t][key] = acc * kh;
       rt.W[T + t][key] = acc * qh;
-      rt.X[t][key] = kh * __builtin_amdgcn_rcpf(acc);  // acc a normal number (bound above)
+      X[t][key] = kh * __builtin_amdgcn_rcpf(acc);  // acc a normal number (bound above)
     }
 #pragma unroll
     for (int m = 2 * T; m < 16; ++m) rt.W[m][key] = 0.0f;
-#pragma unroll
-    for (int m = T; m < 16; ++m) rt.X[m][key] = 0.0f;
   }
   __syncthreads();  // from here q, k, a and g are dead: P, C and o take their space
 
   // 5. P = S0 W (two 16-row tiles per wave) and, on wave 0, C = W X^T.
   //    A operand lane (g, c): W[c][16q + 4g + e]; the K order is shared by
-  //    both operands of each product.
+  //    both operands of each product.  The results stay in registers until
+  //    every wave has passed a barrier: P overlaps the space of X (the gate
+  //    projection's) when T < 6, and wave 0 reads X meanwhile.
   {
-    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f}, cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float4 w4 = *reinterpret_cast<const float4*>(&rt.W[c][16 * q + 4 * g]);
@@ -296,6 +299,19 @@ void kda_record_kernel(const Args A) {
         p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[1][q], e), p1, 0, 0, 0);
       }
     }
+    if (wave == 0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&rt.W[c][16 * q + 4 * g]);
+        // X rows past T are zero operands (columns of C that are never read)
+        const float4 x4 = c < T ? *reinterpret_cast<const float4*>(&X[c][16 * q + 4 * g])
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cc = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(x4, e), cc, 0, 0, 0);
+      }
+    }
+    __syncthreads();
     // D layout (f32 16x16x4): lane l, element r holds D[4(l/16) + r][l%16].
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -303,15 +319,6 @@ void kda_record_kernel(const Args A) {
       sh.u.out.P[4 * g + r][32 * wave + 16 + c] = p1[r];
     }
     if (wave == 0) {
-      f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 w4 = *reinterpret_cast<const float4*>(&rt.W[c][16 * q + 4 * g]);
-        const float4 x4 = *reinterpret_cast<const float4*>(&rt.X[c][16 * q + 4 * g]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          cc = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(x4, e), cc, 0, 0, 0);
-      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) sh.u.out.C[4 * g + r][c] = cc[r];
     }

@@ -116,7 +116,7 @@ def test_ragged_verify(gpu, T):
     check(gpu, p, f"ragged verify T={T}")
 
 
-@pytest.mark.parametrize("T", [2, 8])
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
 def test_record_ragged(gpu, T):
     B, H = 4, 5
     p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=300 + T, record=1))
