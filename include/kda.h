@@ -63,7 +63,8 @@ typedef enum kda_status {
   KDA_ERR_RECORD_T1 = 3,  /* record with T = 1 (the page's assertion) */
   KDA_ERR_NULL = 4,       /* a required pointer is NULL */
   KDA_ERR_SHAPE = 5,      /* B < 0, H < 1, N < 1, W too small, slot_stride < T,
-                             non-finite scalar, or sizes beyond 32-bit grids */
+                             non-finite scalar, or sizes beyond 32-bit grids
+                             (B*H*256 work-items above 2^32 - 1) */
   KDA_ERR_LAUNCH = 6,     /* the kernel launch failed (hipGetLastError) */
   KDA_ERR_ALIGN = 7       /* a pointer not aligned as its operand needs (see the
                              alignment convention above) */

@@ -132,7 +132,9 @@ kda_status kda_replay(const float* rec_u, const uint16_t* rec_kg, const float* a
                       int N, int T, void* stream) {
   if (T < 1 || T > kMaxT) return KDA_ERR_TOKENS;
   if (B < 0 || H < 1 || N < 1 || !isfinite(lower_bound)) return KDA_ERR_SHAPE;
-  if (static_cast<long long>(B) * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+  // B*H workgroups of kThreads work-items: a dispatch counts its grid in
+  // work-items, 32 bits.
+  if (static_cast<long long>(B) * H * kThreads > 0xffffffffLL) return KDA_ERR_SHAPE;
   if (B == 0) return KDA_OK;
   if (!rec_u || !rec_kg || !a_log || !dt_bias || !src_slots || !dst_slots || !n_tokens || !state)
     return KDA_ERR_NULL;

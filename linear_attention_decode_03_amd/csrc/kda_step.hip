@@ -363,8 +363,9 @@ kda_status check(const Args& A, int T, int record, int gate_mode) {
   if (A.W < (T == 1 ? 3 : T + 2)) return KDA_ERR_SHAPE;
   if (T > 1 && A.slot_stride < T) return KDA_ERR_SHAPE;
   if (!isfinite(A.lower_bound) || !isfinite(A.scale) || !isfinite(A.eps)) return KDA_ERR_SHAPE;
-  // Grid and 32-bit index limits: B*H workgroups; H*128 channels per row.
-  if (static_cast<long long>(A.B) * A.H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+  // Grid and 32-bit index limits: B*H workgroups of kThreads work-items (a
+  // dispatch counts its grid in work-items, 32 bits); H*128 channels per row.
+  if (static_cast<long long>(A.B) * A.H * kThreads > 0xffffffffLL) return KDA_ERR_SHAPE;
   if (static_cast<long long>(A.H) * 3 * kD * (T + 3) > 0x7fffffffLL) return KDA_ERR_SHAPE;
   if (A.B == 0) return KDA_OK;
   if (!A.x || !A.conv_w || !A.conv_state || !A.f_a || !A.beta || !A.a_log || !A.dt_bias ||

@@ -71,6 +71,8 @@ OK, TOK, GM, REC, NUL, SHP, ALN = 0, 1, 2, 3, 4, 5, 7
     (dict(B=4, H=2, N=5, W=3, T=1, eps=float("nan")), SHP),
     (dict(B=4, H=2, N=5, W=3, T=1, lower_bound=float("inf")), SHP),
     (dict(B=1 << 20, H=1 << 12, N=5, W=3, T=1), SHP),            # grid beyond 2^31 items
+    (dict(B=1 << 19, H=32, N=5, W=3, T=1), SHP),                 # 2^24 items x 256 = 2^32 work-items
+    (dict(B=(1 << 24) - 1, H=1, N=5, W=3, T=1), OK),             # the largest grid
     # alignment: 16 bytes for state, f_a, f_b; 4 for x, conv_w, conv_b, rec_kg
     (dict(B=4, H=2, N=5, W=3, T=1, pointers={"state": 0x1008}), ALN),
     (dict(B=4, H=2, N=5, W=3, T=1, pointers={"f_a": 0x1004}), ALN),
@@ -132,7 +134,8 @@ def test_replay_rejects_before_device_work(lib):
     P = ctypes.c_void_p
     ptrs = [P(0x1000)] * 8
     for T, B, H, N, want in ((0, 4, 2, 9, TOK), (9, 4, 2, 9, TOK), (4, -1, 2, 9, SHP),
-                             (4, 4, 0, 9, SHP), (4, 4, 2, 0, SHP), (4, 0, 2, 9, OK)):
+                             (4, 4, 0, 9, SHP), (4, 4, 2, 0, SHP), (4, 0, 2, 9, OK),
+                             (4, 1 << 19, 32, 9, SHP)):   # 2^32 work-items
         assert lib.kda_replay(*ptrs, -5.0, B, H, N, T, None) == want
     assert lib.kda_replay(*ptrs, float("nan"), 4, 2, 9, 4, None) == SHP
     nul = list(ptrs)
