@@ -14,6 +14,8 @@ K back-to-back launches of the timed region, divided by K
 second pass); `roofline.cold` times launches each preceded by a 1 GiB
 scratch write, so that no operand is cached (and the caches hold dirty
 lines), `roofline.cold_clean` with a 1 GiB read instead;
+`roofline.copy_ceiling` is what a plain 1 GiB device copy reaches on the
+same GPU;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
@@ -188,6 +190,28 @@ def cpu_baseline_threaded(q, min_seconds=5.0, max_threads=16):
                       f"static split over {n} threads, {el:.1f} s"}
 
 
+def copy_ceiling(torch, reps=10):
+    """What a plain device copy moves on this GPU: 1 GiB copied `reps` times
+    between one pair of events (read + write bytes / time), after one
+    untimed copy."""
+    n = 1 << 28  # 1 GiB of float32
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return {"gbps": 2 * n * 4 / sec / 1e9, "bytes": 2 * n * 4,
+            "what": "1 GiB device-to-device copy (torch copy_), read + write bytes / time"}
+
+
 def run_copy(args):
     import torch
 
@@ -309,6 +333,8 @@ def main():
             out_list.extend(sorted(s_.elapsed_time(e_) for s_, e_ in zip(ev_s, ev_e)))
         del flush
 
+    copy = copy_ceiling(torch) if k_cold else None
+
     items = p["B"] * p["H"]
     abytes = replay_algorithmic_bytes(p) if replay else algorithmic_bytes(p)
     achieved = abytes / (kernel_ms * 1e-3) / 1e9
@@ -351,7 +377,8 @@ def main():
                          "kernel_us_median": clean[k_cold // 2] * 1e3, "launches": k_cold,
                          "achieved": abytes / (clean[k_cold // 2] * 1e-3) / 1e9,
                          "frac": abytes / (clean[k_cold // 2] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                         "evicted_by": "1 GiB read"}},
+                         "evicted_by": "1 GiB read"},
+                     "copy_ceiling": copy},
     }
     result["config"].update(extra)
     if not args.no_cpu:
