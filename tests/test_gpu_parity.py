@@ -124,6 +124,21 @@ def test_record_ragged(gpu, T):
     check(gpu, p, f"record T={T}")
 
 
+@pytest.mark.parametrize("B,T", [(3, 1), (5, 1), (3, 4), (5, 8)])
+def test_many_heads(gpu, B, T):
+    # H = 128: 16384 channels per row of x, gate and out, 49152 convolution
+    # channels; 384 items run the latency kernel, 640 the full-occupancy one
+    H = 128
+    cfg = dict(B=B, H=H, T=T, N=B * T + 2, W=T + 2 if T > 1 else 3, seed=700 + B + T)
+    p = inputs.make_problem(cfg)
+    if B > 3:
+        if T == 1:
+            p["slots"][1] = 0
+        else:
+            p["accepted"][1] = 0
+    check(gpu, p, f"many heads B={B} T={T}")
+
+
 def test_conv_bias(gpu):
     for T in (1, 4):
         cfg = dict(B=3, H=2, T=T, N=3 * T + 2, W=T + 2, seed=400 + T)
