@@ -153,8 +153,9 @@ __device__ __forceinline__ bool resolve(const Args& A, Item& it, SlotRow<T>& slo
 template <int T>
 __device__ __forceinline__ void prefetch_page(const Args& A, float& sink) {
   sink = 0.0f;
-  const int item = static_cast<int>(blockIdx.x) + A.ahead;
-  if (A.ahead <= 0 || item >= static_cast<int>(gridDim.x)) return;
+  const long long next = static_cast<long long>(blockIdx.x) + A.ahead;
+  if (A.ahead <= 0 || next >= static_cast<long long>(gridDim.x)) return;
+  const int item = static_cast<int>(next);
   const int b = item / A.H, h = item % A.H;
   int slot;
   if constexpr (T == 1) {

@@ -441,11 +441,14 @@ kda_status launch(const Args& A, int T, hipStream_t stream) {
 // The prefetch distance: -1 takes the library default (off: the step is at
 // its measured HBM ceiling without it), other values are rounded up to a
 // multiple of 8 so that the prefetching workgroup and the one that reads the
-// page sit on the same XCD.
+// page sit on the same XCD.  A distance of a whole grid or more touches no
+// page; it is capped well below the int range.
 constexpr int kDefaultAhead = 0;
+constexpr int kMaxAhead = 1 << 30;
 
 int resolve_ahead(int ahead) {
   if (ahead < 0) ahead = kDefaultAhead;
+  if (ahead > kMaxAhead) ahead = kMaxAhead;
   return (ahead + 7) & ~7;
 }
 

@@ -184,7 +184,7 @@ def test_prefetch_changes_nothing(gpu, name):
     p = inputs.make_problem(name)
     say(f"[prefetch] {name}")
     base = gpu_step(gpu, copy_problem(p), ahead=0)
-    for ahead in (8, 100, 1024):
+    for ahead in (8, 100, 1024, 2**31 - 1):   # the last: beyond any grid
         got = gpu_step(gpu, copy_problem(p), ahead=ahead)
         for k in ("state", "conv_state", "out", "rec_u", "rec_kg"):
             if base[k] is not None:
