@@ -55,3 +55,15 @@ def test_threaded_oracle_equals_single_thread():
     assert r["cores"] == min(4, len(__import__("os").sched_getaffinity(0)))
     for k in ("state", "conv_state", "out"):
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+
+
+def test_more_than_one_gpu_is_refused():
+    # the step has no cross-GPU exchange; the bench measures one GPU and
+    # says so for any other count (before touching a device)
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
