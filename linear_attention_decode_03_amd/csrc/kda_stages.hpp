@@ -71,8 +71,9 @@ struct Shared {
 
 // Record-mode operand table W: rows A_t k_hat_t (t < T) and A_t q_hat_t
 // (T + t); rows beyond are zero.  (Its X rows, k_hat_t / A_t, live in the
-// space of Inputs::g.)
-struct RecordTables {
+// space of Inputs::g.)  Until W is written its space holds the item's f_a
+// rows in FP64 for the gate projection.
+struct alignas(16) RecordTables {
   float W[16][kPad];
 };
 
@@ -554,6 +555,120 @@ __device__ __forceinline__ void gate_rounds_compute(GateRounds<T>& gr, SH& sh) {
     for (int fg = 0; fg < 2; ++fg) gr.fb[fg] = fb_next[fg];
 #pragma unroll
     for (int tg = 0; tg < kTG; ++tg) gr.fa[tg] = fa_next[tg];
+  }
+#pragma unroll
+  for (int fg = 0; fg < 2; ++fg) {
+    const int f = 32 * wave + 16 * fg + 4 * b + (lane >> 4);
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg) {
+      const int t = 4 * tg + j;
+      if (t < T) sh.u.in.g[t][f] = static_cast<float>(acc[fg][tg]);
+    }
+  }
+}
+
+// The record kernel's variant: the f_a rows of the item are converted to
+// FP64 once, into an LDS table shared by the four waves, so the B operand
+// of every gate step is one 8-byte LDS read instead of a global load and
+// two conversions per lane; only the F_B rows come in rounds.  Column
+// 32k + r of token t sits at t * kFaPitch + 33k + r (doubles): the 16
+// distinct addresses of one read (4 tokens x 4 column quarters) fall in
+// distinct banks.
+constexpr int kFaPitch = 4 * 33;
+
+template <int T>
+struct FaPairs {
+  static constexpr int kPer = (T + 3) / 4;  // tokens per thread
+  uint32_t v[kPer];                         // two BF16 columns of one token
+};
+
+// Thread tid: columns 2(tid & 63) and 2(tid & 63) + 1 of tokens
+// (tid >> 6) + 4m.  Tokens past T - 1 load token T - 1 (no load under a
+// branch) and are not stored.
+template <int T>
+__device__ __forceinline__ void fa_pairs_load(const Args& A, const Item& it, FaPairs<T>& fp) {
+  const int pc = threadIdx.x & 63, tt = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < FaPairs<T>::kPer; ++m) {
+    const int t = tt + 4 * m;
+    const int tok = t < T ? t : T - 1;
+    fp.v[m] = *reinterpret_cast<const uint32_t*>(A.f_a + (it.token0 + tok) * kD + 2 * pc);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void fa_pairs_store(const FaPairs<T>& fp, double* fa64) {
+  const int pc = threadIdx.x & 63, tt = threadIdx.x >> 6;
+  const int col = 2 * pc;
+  const int at = 33 * (col >> 5) + (col & 31);
+#pragma unroll
+  for (int m = 0; m < FaPairs<T>::kPer; ++m) {
+    const int t = tt + 4 * m;
+    if (t < T) {
+      fa64[t * kFaPitch + at] = static_cast<double>(bf16_lo(fp.v[m]));
+      fa64[t * kFaPitch + at + 1] = static_cast<double>(bf16_hi(fp.v[m]));
+    }
+  }
+}
+
+template <int T>
+struct GateRoundsFB {
+  const uint16_t* fb_base;  // wave-uniform
+  uint32_t fb_off;          // lane offset in elements
+  uint4 fb[2];              // the current round
+};
+
+template <int T>
+__device__ __forceinline__ void gate_fb_rounds_begin(const Args& A, const Item& it,
+                                                     GateRoundsFB<T>& gr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int k = lane >> 4, b = (lane >> 2) & 3, i = lane & 3;
+  gr.fb_base = A.f_b + static_cast<size_t>(it.h) * kD * kD;
+  gr.fb_off = (32 * wave + 4 * b + i) * kD + 32 * k;  // feature group 1: 16 rows on
+#pragma unroll
+  for (int fg = 0; fg < 2; ++fg)
+    gr.fb[fg] = *reinterpret_cast<const uint4*>(gr.fb_base + gr.fb_off + 16 * kD * fg);
+}
+
+template <int T, class SH>
+__device__ __forceinline__ void gate_fb_rounds_compute(GateRoundsFB<T>& gr, const double* fa64,
+                                                       SH& sh) {
+  constexpr int kTG = GateQuadOperands<T>::kTokenGroups;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int k = lane >> 4, b = (lane >> 2) & 3, j = lane & 3;
+  int row[kTG];
+#pragma unroll
+  for (int tg = 0; tg < kTG; ++tg) {
+    const int tok = 4 * tg + j < T ? 4 * tg + j : T - 1;
+    row[tg] = tok * kFaPitch + 33 * k;
+  }
+  double acc[2][kTG];
+#pragma unroll
+  for (int fg = 0; fg < 2; ++fg)
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg) acc[fg][tg] = 0.0;
+#pragma unroll 1
+  for (int n = 0; n < 4; ++n) {
+    const uint32_t col = 8 * (n < 3 ? n + 1 : n);
+    uint4 fb_next[2];
+#pragma unroll
+    for (int fg = 0; fg < 2; ++fg)
+      fb_next[fg] = *reinterpret_cast<const uint4*>(gr.fb_base + gr.fb_off + 16 * kD * fg + col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double bv[kTG];
+#pragma unroll
+      for (int tg = 0; tg < kTG; ++tg) bv[tg] = fa64[row[tg] + 8 * n + e];
+#pragma unroll
+      for (int fg = 0; fg < 2; ++fg) {
+        const double av = static_cast<double>(bf16_at(gr.fb[fg], e));
+#pragma unroll
+        for (int tg = 0; tg < kTG; ++tg)
+          acc[fg][tg] = __builtin_amdgcn_mfma_f64_4x4x4f64(av, bv[tg], acc[fg][tg], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int fg = 0; fg < 2; ++fg) gr.fb[fg] = fb_next[fg];
   }
 #pragma unroll
   for (int fg = 0; fg < 2; ++fg) {

@@ -218,8 +218,10 @@ void kda_record_kernel(const Args A) {
   locate<T>(A, it);
   ConvOperands<T> co;
   conv_load_inputs<T, kBias>(A, it, co);
-  GateRounds<T> gr;
-  gate_rounds_begin<T>(A, it, gr);
+  GateRoundsFB<T> gr;
+  gate_fb_rounds_begin<T>(A, it, gr);
+  FaPairs<T> fp;
+  fa_pairs_load<T>(A, it, fp);
   const float beta_logit = load_beta<T>(A, it);
   const float dt = load_dt(A, it);
   __builtin_amdgcn_sched_barrier(0);
@@ -234,11 +236,16 @@ void kda_record_kernel(const Args A) {
   const int g = lane >> 4, c = lane & 15;
   conv_load_taps<T, kConvF32>(A, it, co);
   __builtin_amdgcn_sched_barrier(0);
+  // f_a in FP64 for the gate, in the space of W (written only in step 4)
+  static_assert(T * kFaPitch * sizeof(double) <= sizeof(rt.W), "f_a table exceeds W");
+  double* fa64 = reinterpret_cast<double*>(&rt.W[0][0]);
+  fa_pairs_store<T>(fp, fa64);
+  __syncthreads();
 
   // 2. Convolution, norms, gate projection.
   conv_compute<T, true, kConvF32>(A, it, sh, co);
   store_beta<T>(sh, beta_logit);
-  gate_rounds_compute<T>(gr, sh);
+  gate_fb_rounds_compute<T>(gr, fa64, sh);
   OutputOperands<T> oo;
   load_output_operands<T>(A, it, oo);
   __syncthreads();
