@@ -76,8 +76,10 @@ __device__ __forceinline__ float silu_bf16(float x) {
   const float yf = x * __builtin_amdgcn_rcpf(1.0f + ef);
   const uint32_t bits = __float_as_uint(yf);
   const int dist = abs(static_cast<int>(bits & 0xffffu) - 0x8000);
-  const int margin = static_cast<int>(2.0f * fminf(ax, 80.0f)) + 16;
-  if (ax < 80.0f && dist > margin) return round_bf16(yf);
+  // Both tests without a branch between them (the fast value is computed
+  // for every x; v_exp_f32 and v_rcp_f32 take any argument).
+  const bool fast = (ax < 80.0f) & (static_cast<float>(dist) > fmaf(2.0f, ax, 16.0f));
+  if (fast) return round_bf16(yf);
   return silu_bf16_exact(x);
 }
 
