@@ -168,6 +168,46 @@ def test_replay_deterministic(gpu):
     assert np.array_equal(got[0].view(np.uint8), got[1].view(np.uint8))
 
 
+def test_largest_grid(gpu):
+    # B*H = 2^24 - 1 items (H = 1): the largest grid the host checks accept
+    # (B*H*256 work-items below 2^32).  One live request near the end of
+    # the grid on slot 1 of a 2-slot pool, every other request padding;
+    # operands (~26 GB) are made on the device.  The live item is compared
+    # with the oracle on that request alone (items are independent), every
+    # other output row must be +0.
+    import torch
+
+    from linear_attention_decode_03_amd import kda
+
+    B, live = (1 << 24) - 1, (1 << 24) - 5
+    small = inputs.make_problem(dict(B=1, H=1, T=1, N=2, W=3, seed=1201))
+    before = copy_problem(small)
+    ref = copy_problem(small)
+    taps = oracle.run(ref, taps=True)
+    d = gpu.to_device(small)
+    say(f"[largest grid] B={B} H=1, live request {live}")
+    big = {}
+    for k in ("x", "f_a", "beta", "gate"):
+        t = d[k]
+        big[k] = torch.zeros((B,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+        big[k][live] = t[0]
+    slots = torch.zeros(B, dtype=torch.int32, device="cuda")
+    slots[live] = 1
+    out = torch.full((B, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kda.kda_decode(big["x"], d["conv_w"], d["conv_b"], d["conv_state"], big["f_a"], big["beta"],
+                   d["a_log"], d["dt_bias"], slots, d["state"], out, big["gate"], d["norm_w"],
+                   small["lower_bound"], small["scale"], small["eps"], d["f_b"])
+    torch.cuda.synchronize()
+    got = gpu.to_host(dict(state=d["state"], conv_state=d["conv_state"], out=out[live:live + 1],
+                           rec_u=None, rec_kg=None))
+    _parity.compare_step(before, ref, got, taps)
+    bits = out.view(torch.int16)
+    bits[live] = 0
+    assert int(torch.count_nonzero(bits)) == 0, "a padded row is not +0"
+    del big, slots, out, bits
+    torch.cuda.empty_cache()
+
+
 def test_conv_bias(gpu):
     for T in (1, 4):
         cfg = dict(B=3, H=2, T=T, N=3 * T + 2, W=T + 2, seed=400 + T)
