@@ -352,8 +352,12 @@ __device__ __forceinline__ void store_beta(SH& sh, float beta_logit) {
   if (threadIdx.x < T) sh.beta[threadIdx.x] = sigmoid_fast(beta_logit);
 }
 
-// Gate projection raw_g[t][f] = BF16(sum_j F_B[h*128+f][j] f_a[t][j]), exact:
-// the products of two BF16 values are exact and are summed in FP64.
+// Gate projection raw_g[t][f] = BF16(sum_j F_B[h*128+f][j] f_a[t][j]): the
+// products of two BF16 values (16 significant bits) are exact in FP64 and
+// are summed in FP64.  The sum is exact while the 128 products span fewer
+// than 2^37 in magnitude (53 bits hold every partial sum); beyond that each
+// addition errs by at most 2^-53 relative, so the order of the sum could
+// change the FP32 rounding only within ~2^-45 of a rounding boundary.
 // One token (decode): on the vector ALUs.  Thread holds features
 // 16i + (tid >> 4) and columns 8(tid & 15) .. +7 (every 16-byte load of the
 // workgroup contiguous); a feature's 16 partial sums sit in one 16-lane row.
@@ -373,22 +377,21 @@ __device__ __forceinline__ void gate_load(const Args& A, const Item& it, GateOpe
   go.fa = *reinterpret_cast<const uint4*>(A.f_a + it.token0 * kD + j0);
 }
 
+// Both factors are widened to FP64 before they meet (an FP64 fma): the
+// product of two BF16 values is then exact for every finite input, also
+// where an FP32 product would underflow or overflow.
 template <class SH>
 __device__ __forceinline__ void gate_valu(const GateOperands& go, SH& sh) {
   const int tid = threadIdx.x;
   const int fsub = tid >> 4;
-  const uint4 fa4 = go.fa;
+  double fa[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) fa[e] = static_cast<double>(bf16_at(go.fa, e));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint4 fb = go.fb[i];
-    double acc = static_cast<double>(bf16_lo(fb.x) * bf16_lo(fa4.x));
-    acc += static_cast<double>(bf16_hi(fb.x) * bf16_hi(fa4.x));
-    acc += static_cast<double>(bf16_lo(fb.y) * bf16_lo(fa4.y));
-    acc += static_cast<double>(bf16_hi(fb.y) * bf16_hi(fa4.y));
-    acc += static_cast<double>(bf16_lo(fb.z) * bf16_lo(fa4.z));
-    acc += static_cast<double>(bf16_hi(fb.z) * bf16_hi(fa4.z));
-    acc += static_cast<double>(bf16_lo(fb.w) * bf16_lo(fa4.w));
-    acc += static_cast<double>(bf16_hi(fb.w) * bf16_hi(fa4.w));
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fma(static_cast<double>(bf16_at(go.fb[i], e)), fa[e], acc);
     acc = row_sum16_f64(acc);
     if ((tid & 15) == 0) sh.u.in.g[0][16 * i + fsub] = static_cast<float>(acc);
   }

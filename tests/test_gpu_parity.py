@@ -247,6 +247,14 @@ def test_conv_f32_ragged_bias(gpu, T):
     check(gpu, p, f"conv_f32 bias T={T}")
 
 
+@pytest.mark.parametrize("name,ahead", [("decode_b256", 256), ("verify_t4", 64),
+                                        ("decode_b64", 1024), ("verify_record_t8", 8)])
+def test_prefetch_parity(gpu, name, ahead):
+    """With the prefetch on, the step matches the oracle (the full workload,
+    every item compared)."""
+    check(gpu, inputs.make_problem(name), f"{name} ahead={ahead}", ahead=ahead)
+
+
 @pytest.mark.parametrize("name", ["decode_b64", "verify_t4", "verify_record_t8"])
 def test_prefetch_changes_nothing(gpu, name):
     """The prefetch distance is a hint: every value gives identical bits."""

@@ -20,6 +20,24 @@ SRC = os.path.join(ROOT, "oracle", "kda_oracle.c")
 # (name, exact text in the oracle, replacement)
 MUTANTS = [
     ("conv tap order reversed", "window[p][c][t + i]", "window[p][c][t + 3 - i]"),
+    ("conv chain accumulated from the last tap", "for (int i = 0; i < TAPS; ++i) {",
+     "for (int i = TAPS - 1; i >= 0; --i) {"),
+    ("conv chain with a separate multiply and add", "acc = fmaf(window[p][c][t + i], w, acc);",
+     "acc = window[p][c][t + i] * w + acc;"),
+    ("conv bias added after the taps",
+     "float acc = P->has_bias ? bf16_to_float(P->conv_b[ch]) : 0.0f;\n"
+     "        for (int i = 0; i < TAPS; ++i) {\n"
+     "          float w = bf16_to_float(P->conv_w[((size_t)p * TAPS + i) * dim + (size_t)h * D + c]);\n"
+     "          acc = fmaf(window[p][c][t + i], w, acc);\n"
+     "        }\n",
+     "float acc = 0.0f;\n"
+     "        for (int i = 0; i < TAPS; ++i) {\n"
+     "          float w = bf16_to_float(P->conv_w[((size_t)p * TAPS + i) * dim + (size_t)h * D + c]);\n"
+     "          acc = fmaf(window[p][c][t + i], w, acc);\n"
+     "        }\n"
+     "        acc = acc + (P->has_bias ? bf16_to_float(P->conv_b[ch]) : 0.0f);\n"),
+    ("q scale folded into the norm factor", "q_hat[t][c] = (Y[0][t][c] * fq) * P->scale;",
+     "q_hat[t][c] = Y[0][t][c] * (fq * P->scale);"),
     ("conv weight of wrong head",
      "((size_t)p * TAPS + i) * dim + (size_t)h * D + c]", "((size_t)p * TAPS + i) * dim + c]"),
     ("conv window starts at column 0", "size_t at = base + off + i;", "size_t at = base + i;"),

@@ -354,6 +354,118 @@ def test_conv_f32_reduces_to_bf16(oracle_lib, T):
     assert np.array_equal(q["conv_state"], from_bf16(p["conv_state"]).reshape(p["conv_state"].shape))
 
 
+# The kernel body accumulates the convolution as one FP32 chain that starts
+# at the bias (or 0) and takes an fma with the weight of tap i = 0, 1, 2, 3 in
+# turn (the convolution block, stock tap order).  The cases below are built
+# by hand so that the chain's order and its fused multiply-add show in the
+# BF16 result; any other order or a separate multiply and add lands on a
+# different value.
+BIG = float(2 ** 24)  # 2^24 + 1 is a tie in FP32 and rounds to 2^24 (even)
+
+
+def _conv_window_setter(p, part, b, h):
+    """Returns a function set(col, value) that writes window column `col`
+    (0-2: the pool taps at off + col, 3 + t: input x_t) of every channel of
+    `part` of item (b, h)."""
+    T, dim = p["T"], p["H"] * D
+    off = 0 if T == 1 else int(p["accepted"][b]) - 1
+    cs = int(p["slots"][b]) if T == 1 else int(p["slots"][b, 0])
+    ch = part * dim + h * D + np.arange(D)
+
+    def put(col, value):
+        if col < 3:
+            if p.get("conv_f32"):
+                p["conv_state"][cs, ch, off + col] = np.float32(value)
+            else:
+                p["conv_state"][cs, ch, off + col] = to_bf16(np.float32(value))
+        else:
+            p["x"][b * T + col - 3, ch] = to_bf16(np.float32(value))
+    return put
+
+
+@pytest.mark.parametrize("T,t", [(1, 0), (3, 0), (3, 1), (5, 2)])
+def test_conv_chain_order_bf16(oracle_lib, T, t):
+    """Window [.., 2^24, 1, -2^24, 1 ..] at positions t .. t+3, weights all 1:
+    the chain i = 0..3 gives ((2^24 + 1) - 2^24) + 1 = 1 (the first add
+    rounds away the 1); the reversed chain gives ((1 - 2^24) + 1) + 2^24 = 2
+    (every step exact).  So k = BF16(silu(1)), not BF16(silu(2))."""
+    p = small(T=T, B=2, H=2, seed=71 + T)
+    if T > 1:
+        p["accepted"][:] = 1
+    set_conv_taps(p, 1, [1, 1, 1, 1])
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            put = _conv_window_setter(p, 1, b, h)
+            for i, value in enumerate((BIG, 1.0, -BIG, 1.0)):
+                put(t + i, value)
+    taps = oracle_lib.run(p, taps=True)
+    want = bf16_of_f64(silu64(1.0))
+    assert want != bf16_of_f64(silu64(2.0))
+    assert np.all(taps["k"][:, :, t, :] == want)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_conv_chain_starts_at_bias(oracle_lib, T):
+    """Bias 2^24 and window [1, -2^24, 0, 0]: starting from the bias,
+    (2^24 + 1) rounds to 2^24 and the chain ends at 0; a bias added after
+    the taps would give (1 - 2^24) + 2^24 = 1."""
+    p = small(T=T, B=2, H=2, seed=81 + T)
+    if T > 1:
+        p["accepted"][:] = 1
+    dim = p["H"] * D
+    p["has_bias"] = 1
+    bias = np.zeros(3 * dim, np.float32)
+    bias[dim:2 * dim] = BIG
+    p["conv_b"] = to_bf16(bias)
+    set_conv_taps(p, 1, [1, 1, 1, 1])
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            put = _conv_window_setter(p, 1, b, h)
+            for i, value in enumerate((1.0, -BIG, 0.0, 0.0)):
+                put(i, value)
+    taps = oracle_lib.run(p, taps=True)
+    assert np.all(taps["k"][:, :, 0, :] == 0.0)
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_conv_chain_is_fused_fp32_pool(oracle_lib, T):
+    """FP32 pool: taps [-(1 + 2^-7 + 2^-23), 1 + 2^-23, 0], weights
+    [1, 1 + 2^-7, 0, 0].  The second product is 1 + 2^-7 + 2^-23 + 2^-30;
+    an fma keeps it exactly, so the chain leaves 2^-30 and k = BF16(silu(2^-30));
+    a product rounded to FP32 first loses the 2^-30 and would give 0."""
+    p = small(T=T, B=2, H=2, seed=91 + T, conv_f32=1)
+    if T > 1:
+        p["accepted"][:] = 1
+    set_conv_taps(p, 1, [1.0, 1.0 + 2.0 ** -7, 0.0, 0.0])
+    a = -(1.0 + 2.0 ** -7 + 2.0 ** -23)
+    for b in range(p["B"]):
+        for h in range(p["H"]):
+            put = _conv_window_setter(p, 1, b, h)
+            for i, value in enumerate((a, 1.0 + 2.0 ** -23, 0.0)):
+                put(i, value)
+    taps = oracle_lib.run(p, taps=True)
+    want = bf16_of_f64(silu64(2.0 ** -30))
+    assert want > 0
+    assert np.all(taps["k"][:, :, 0, :] == want)
+
+
+def test_q_scale_applied_after_the_norm_factor(oracle_lib):
+    """q_hat = (q * fq) * scale, two FP32 products in that order (kernel
+    body, normalised q): then q_hat at scale s is exactly the FP32 product
+    of q_hat at scale 1 and s.  Multiplying q by the FP32 product fq * s
+    instead breaks that relation for some channels."""
+    p = small(B=4, H=2, seed=95)
+    s = np.float32(0.0883883476)
+    q1 = inputs.copy_problem(p)
+    q1["scale"] = 1.0
+    qs = inputs.copy_problem(p)
+    qs["scale"] = float(s)
+    t1 = oracle_lib.run(q1, taps=True)
+    ts = oracle_lib.run(qs, taps=True)
+    want = (t1["q_hat"].astype(np.float32) * s).astype(np.float32)
+    assert np.array_equal(ts["q_hat"].view(np.uint32), want.view(np.uint32))
+
+
 def test_gate_one_hot(oracle_lib):
     """One-hot F_B rows: raw_g[f] = f_a[pi(f)] bit for bit (record output)."""
     T = 2
