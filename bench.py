@@ -21,6 +21,7 @@ same GPU;
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                     [--cold-launches C]
     python bench.py --mode copy      # 1 GiB device copies (counter calibration)
+    python bench.py --mode sweep     # small batches, unsplit vs split (graph replay)
 
 Workloads: tiny_decode, decode_b64, decode_b256 (default), verify_t4,
 verify_record_t8 (the step), and replay_t8 (the RecoverSSM replay of
@@ -230,6 +231,66 @@ def run_copy(args):
                       "gbps": 2 * n * 4 * args.steps / el / 1e9}))
 
 
+def run_sweep(args):
+    """Small batches: per-launch time of decode (T=1) and verify (T=2, 4, 8)
+    at H=32 and B*H in {32 .. 2048} items, unsplit and split over 2 and 4
+    workgroups per item.  Each configuration captures 20 launches in one HIP
+    graph (so host launch overhead is out of the figure) and replays it;
+    the median over 15 timed replays, divided by 20, is printed per
+    configuration as one JSON line."""
+    import torch
+
+    from linear_attention_decode_03_amd import inputs, kda
+    from linear_attention_decode_03_amd import device as dev
+
+    kda.load_library()
+    H = 32
+    for T in (1, 2, 4, 8):
+        for items in (32, 64, 128, 256, 512, 1024, 2048):
+            B = items // H
+            cfg = dict(B=B, H=H, T=T, seed=11, N=(2 * B + 2) if T == 1 else B * T + 1,
+                       W=3 if T == 1 else T + 2)
+            p = inputs.make_problem(cfg)
+            row = {"mode": "sweep", "T": T, "items": items}
+            for split in (1, 2, 4):
+                if split > 1 and items * split > 2048:
+                    continue
+                d = dev.to_device(p)
+                ws = kda.split_workspace(B, H, T, d["state"].device)
+
+                def step():
+                    if split == 1:
+                        dev.run(d)
+                    else:
+                        dev.run_split(d, ws, split=split)
+
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    for _ in range(3):
+                        step()
+                torch.cuda.current_stream().wait_stream(s)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(20):
+                        step()
+                g.replay()
+                torch.cuda.synchronize()
+                times = []
+                for _ in range(15):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1) * 1e3 / 20)
+                row[f"split{split}_us"] = sorted(times)[len(times) // 2]
+                del g, d, ws
+            print(json.dumps(row), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,7 +302,7 @@ def main():
     ap.add_argument("--cold-launches", type=int, default=20)
     ap.add_argument("--conv-f32", action="store_true",
                     help="keep the convolution pool in FP32 (kda_*_f32conv)")
-    ap.add_argument("--mode", choices=["kda", "copy"], default="kda")
+    ap.add_argument("--mode", choices=["kda", "copy", "sweep"], default="kda")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -253,9 +314,11 @@ def main():
 
     if args.mode == "copy":
         return run_copy(args)
+    if args.mode == "sweep":
+        return run_sweep(args)
 
+    from linear_attention_decode_03_amd import device as _gpu
     from linear_attention_decode_03_amd import inputs, kda
-    from tests import _gpu
 
     kda.load_library()
     replay = args.workload in inputs.REPLAY_CONFIGS

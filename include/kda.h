@@ -46,6 +46,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -66,8 +67,10 @@ typedef enum kda_status {
                              non-finite scalar, or sizes beyond 32-bit grids
                              (B*H*256 work-items above 2^32 - 1) */
   KDA_ERR_LAUNCH = 6,     /* the kernel launch failed (hipGetLastError) */
-  KDA_ERR_ALIGN = 7       /* a pointer not aligned as its operand needs (see the
+  KDA_ERR_ALIGN = 7,      /* a pointer not aligned as its operand needs (see the
                              alignment convention above) */
+  KDA_ERR_WORKSPACE = 8   /* a split call's workspace is NULL, smaller than
+                             kda_split_workspace_bytes or not 4-byte aligned */
 } kda_status;
 
 /*
@@ -169,6 +172,54 @@ kda_status kda_verify_f32conv(const uint16_t* x, const uint16_t* conv_w,
                               const int32_t* accepted, float* rec_u, uint16_t* rec_kg, int B,
                               int H, int N, int W, int T, int slot_stride, int record,
                               int gate_mode, int ahead, void* stream);
+
+/*
+ * kda_decode_split, kda_verify_split -- kda_decode and kda_verify (plain
+ * verify, no record mode) for small batches: each (request, head) item is
+ * split over `split` workgroups, each owning 128/split value rows of the
+ * state (the KdaSplit of the KdaWide class docstring, which spreads a head
+ * over several CTAs when there are few requests).  The results are those of
+ * kda_decode / kda_verify (the same roundings; only the FP32 order of the
+ * recurrence's dot products may differ).  Operands, layouts, ownership,
+ * errors and caller contract as for kda_decode / kda_verify, with a BF16
+ * convolution pool, plus:
+ *   split      workgroups per item: 2 or 4; 1 runs the unsplit kernels
+ *              (kda_decode / kda_verify with the default prefetch); 0 lets
+ *              the library choose from B*H and T (measured on MI355X: no
+ *              split below 4 tokens; for T >= 4, 4 up to 64 items, 2 up to
+ *              128, 1 above).  Other values: KDA_ERR_SHAPE.
+ *   workspace  device memory of at least kda_split_workspace_bytes(B, H, T)
+ *              bytes, 4-byte aligned.  Its first B*H 32-bit words are one
+ *              counter per item and must be ZERO before the first use; every
+ *              launch leaves them zero again when it completes, so one
+ *              workspace serves any number of calls in a stream.  The rest
+ *              holds the items' recurrence outputs between the workgroups of
+ *              an item (no initial value needed).  Calls that may run at the
+ *              same time (other streams) need workspaces of their own.  Not
+ *              read when the chosen split is 1 (may then be NULL).
+ * The last workgroup of an item to finish writes the item's convolution
+ * window and its normalised output; the workgroups hand over through
+ * atomics on the workspace, with no waiting.  kda_split_workspace_bytes
+ * returns 0 for B or H below 1 or T outside [1, 8].
+ */
+size_t kda_split_workspace_bytes(int B, int H, int T);
+
+kda_status kda_decode_split(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                            uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                            const float* a_log, const float* dt_bias, const int32_t* slots,
+                            float* state, uint16_t* out, const uint16_t* gate,
+                            const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                            const uint16_t* f_b, int B, int H, int N, int W, int gate_mode,
+                            int split, void* workspace, size_t workspace_bytes, void* stream);
+
+kda_status kda_verify_split(const uint16_t* x, const uint16_t* conv_w, const uint16_t* conv_b,
+                            uint16_t* conv_state, const uint16_t* f_a, const uint16_t* beta,
+                            const float* a_log, const float* dt_bias, const int32_t* slots,
+                            float* state, uint16_t* out, const uint16_t* gate,
+                            const uint16_t* norm_w, float lower_bound, float scale, float eps,
+                            const uint16_t* f_b, const int32_t* accepted, int B, int H, int N,
+                            int W, int T, int slot_stride, int gate_mode, int split,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_replay -- RecoverSSM: the state after the first n accepted tokens of a

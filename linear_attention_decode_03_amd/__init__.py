@@ -6,5 +6,5 @@ libkda.so next to this file.  `kda` is the thin ctypes binding; `inputs`
 makes seeded synthetic operands.  Importing the package loads nothing.
 """
 
-from .kda import (kda_decode, kda_replay, kda_status_string, kda_validate, kda_verify,  # noqa: F401
-                  load_library)
+from .kda import (kda_decode, kda_decode_split, kda_replay, kda_status_string,  # noqa: F401
+                  kda_validate, kda_verify, kda_verify_split, load_library, split_workspace)

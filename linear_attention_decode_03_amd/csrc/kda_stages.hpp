@@ -102,17 +102,23 @@ __device__ __forceinline__ int row_slot(const SlotRow<T>& row, int t) {
   return s;
 }
 
-// The item of this workgroup (head-fastest numbering) and its token rows.
+// Item `item` (head-fastest numbering: item = b * H + h) and its token rows.
 template <int T>
-__device__ __forceinline__ void locate(const Args& A, Item& it) {
+__device__ __forceinline__ void locate_item(const Args& A, Item& it, int item) {
   const int H = A.H;
-  it.h = blockIdx.x % H;
-  it.b = blockIdx.x / H;
+  it.h = item % H;
+  it.b = item / H;
   it.dim = H * kD;
   it.token0 = static_cast<size_t>(it.b) * T;
   it.off = 0;
   it.rs = 0;
   it.cs = 0;
+}
+
+// The item of this workgroup.
+template <int T>
+__device__ __forceinline__ void locate(const Args& A, Item& it) {
+  locate_item<T>(A, it, blockIdx.x);
 }
 
 // Slot resolution (uniform over the workgroup); false means padding.  Verify
@@ -279,15 +285,11 @@ __device__ __forceinline__ void conv_load_taps(const Args& A, const Item& it,
 
 // The window is rewritten in place after it was read: [tap1, tap2, x_0 ..]
 // in the pool's type (an FP32 pool receives the inputs' exact FP32 values).
-// The outputs go to the q, k and v tables; record mode stores k.
-template <int T, bool kRecord, bool kConvF32, class SH>
-__device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& sh,
-                                             const ConvOperands<T>& co) {
-  const int part = conv_wave();
-  if (part == 3) return;  // issued copies of wave 2's loads only
-  const int lane = threadIdx.x & 63;
-  const size_t hc = static_cast<size_t>(it.h) * kD + 2 * lane;
-  const size_t ch = static_cast<size_t>(part) * it.dim + hc;
+// Part `part` (wave), channel pair of lane `lane`.
+template <int T, bool kConvF32>
+__device__ __forceinline__ void conv_window_store(const Args& A, const Item& it,
+                                                  const ConvOperands<T>& co, int part, int lane) {
+  const size_t ch = static_cast<size_t>(part) * it.dim + static_cast<size_t>(it.h) * kD + 2 * lane;
   {
     const size_t base = (static_cast<size_t>(it.cs) * 3 * it.dim + ch) * A.W;
 #pragma unroll
@@ -308,6 +310,27 @@ __device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& 
       }
     }
   }
+}
+
+// The whole window of the item, by the three waves that hold its parts.
+template <int T, bool kConvF32>
+__device__ __forceinline__ void conv_write_window(const Args& A, const Item& it,
+                                                  const ConvOperands<T>& co) {
+  const int part = conv_wave();
+  if (part == 3) return;
+  conv_window_store<T, kConvF32>(A, it, co, part, threadIdx.x & 63);
+}
+
+// The convolution outputs go to the q, k and v tables; record mode stores k.
+// kWindow: rewrite the window here (a kernel whose window another workgroup
+// may still read rewrites it later with conv_write_window).
+template <int T, bool kRecord, bool kConvF32, bool kWindow = true, class SH>
+__device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& sh,
+                                             const ConvOperands<T>& co) {
+  const int part = conv_wave();
+  if (part == 3) return;  // issued copies of wave 2's loads only
+  const int lane = threadIdx.x & 63;
+  if constexpr (kWindow) conv_window_store<T, kConvF32>(A, it, co, part, lane);
   float* dst = part == 0 ? &sh.u.in.q[0][0] : part == 1 ? &sh.u.in.k[0][0] : &sh.v[0][0];
 #pragma unroll
   for (int t = 0; t < T; ++t) {

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 HEAD_DIM = 128
 
 KDA_OK, KDA_ERR_TOKENS, KDA_ERR_GATE_MODE, KDA_ERR_RECORD_T1, KDA_ERR_NULL, KDA_ERR_SHAPE, \
-    KDA_ERR_LAUNCH, KDA_ERR_ALIGN = range(8)
+    KDA_ERR_LAUNCH, KDA_ERR_ALIGN, KDA_ERR_WORKSPACE = range(9)
 
 _lib = None
 _P = ctypes.c_void_p
@@ -58,6 +58,12 @@ def load_library(path: str = LIB_PATH):
         lib.kda_validate.argtypes = _OPERANDS + [_P] * 3 + [_I] * 8
         lib.kda_replay.restype = _I
         lib.kda_replay.argtypes = [_P] * 8 + [_F] + [_I] * 4 + [_P]
+        lib.kda_split_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_split_workspace_bytes.argtypes = [_I, _I, _I]
+        lib.kda_decode_split.restype = _I
+        lib.kda_decode_split.argtypes = _OPERANDS + [_I] * 6 + [_P, ctypes.c_size_t, _P]
+        lib.kda_verify_split.restype = _I
+        lib.kda_verify_split.argtypes = _OPERANDS + [_P] + [_I] * 8 + [_P, ctypes.c_size_t, _P]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [_I]
         _lib = lib
@@ -215,6 +221,81 @@ def kda_verify(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, 
             _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
             _ptr(accepted), _ptr(rec_u), _ptr(rec_kg), B, H, N, W, T, int(slots.shape[1]),
             int(bool(record)), int(gate_mode), int(ahead), _stream(stream, state.device))
+    _raise(status)
+
+
+def split_workspace(B, H, T, device):
+    """A zero-filled workspace for kda_decode_split / kda_verify_split with B
+    requests of H heads and T tokens; calls leave its counters zero, so it
+    can be kept and reused on one stream."""
+    import torch
+
+    n = int(load_library().kda_split_workspace_bytes(int(B), int(H), int(T)))
+    return torch.zeros(max(1, n // 4), dtype=torch.int32, device=device)
+
+
+def _workspace(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def kda_decode_split(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                     out, gate, norm_w, lower_bound, scale, eps, f_b, workspace, split=0,
+                     gate_mode=0, stream=None):
+    """One decode step with each item split over `split` workgroups (0: the
+    library chooses); see kda_decode_split in include/kda.h.  `workspace`:
+    a tensor from split_workspace (zero-filled device memory)."""
+    import torch
+
+    B, H, N, W = _sizes(x, state, conv_state, 1)
+    _check_common(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
+                  gate, norm_w, f_b, B, H, 1)
+    if conv_state.dtype != torch.bfloat16:
+        raise ValueError("conv_state: the split step takes a BF16 convolution pool")
+    if workspace is not None:
+        _check("workspace", workspace, workspace.dtype, 1, state.device)
+    ws, ws_bytes = _workspace(workspace)
+    with torch.cuda.device(state.device):
+        status = load_library().kda_decode_split(
+            _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
+            _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
+            _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
+            B, H, N, W, int(gate_mode), int(split), ws, ws_bytes, _stream(stream, state.device))
+    _raise(status)
+
+
+def kda_verify_split(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                     out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, workspace,
+                     T=None, split=0, gate_mode=0, stream=None):
+    """One plain verify step (no record mode) with each item split over
+    `split` workgroups (0: the library chooses); see kda_verify_split in
+    include/kda.h."""
+    import torch
+
+    if slots.dim() != 2:
+        raise ValueError("slots: expected [B, slot_stride]")
+    T = int(T if T is not None else slots.shape[1])
+    if not 1 <= T <= 8:
+        _raise(KDA_ERR_TOKENS)
+    B, H, N, W = _sizes(x, state, conv_state, T)
+    _check_common(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
+                  gate, norm_w, f_b, B, H, T)
+    if conv_state.dtype != torch.bfloat16:
+        raise ValueError("conv_state: the split step takes a BF16 convolution pool")
+    _check("accepted", accepted, torch.int32, 1, state.device)
+    if accepted.shape[0] != B:
+        raise ValueError("accepted: expected [B]")
+    if workspace is not None:
+        _check("workspace", workspace, workspace.dtype, 1, state.device)
+    ws, ws_bytes = _workspace(workspace)
+    with torch.cuda.device(state.device):
+        status = load_library().kda_verify_split(
+            _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
+            _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
+            _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
+            _ptr(accepted), B, H, N, W, T, int(slots.shape[1]), int(gate_mode), int(split),
+            ws, ws_bytes, _stream(stream, state.device))
     _raise(status)
 
 

@@ -28,26 +28,27 @@ def lib():
 
 def declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:kda_status|const char\s*\*)\s*(kda_\w+)\s*\(", text,
-                                 flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:kda_status|size_t|const char\s*\*)\s*(kda_\w+)\s*\(",
+                                 text, flags=re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert names == ["kda_decode", "kda_decode_f32conv", "kda_replay", "kda_status_string",
-                     "kda_validate", "kda_verify", "kda_verify_f32conv"]
+    assert names == ["kda_decode", "kda_decode_f32conv", "kda_decode_split", "kda_replay",
+                     "kda_split_workspace_bytes", "kda_status_string", "kda_validate",
+                     "kda_verify", "kda_verify_f32conv", "kda_verify_split"]
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = kda.kda_status_string(code)
         assert s and s != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
 
 
-OK, TOK, GM, REC, NUL, SHP, ALN = 0, 1, 2, 3, 4, 5, 7
+OK, TOK, GM, REC, NUL, SHP, ALN, WSP = 0, 1, 2, 3, 4, 5, 7, 8
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -128,6 +129,46 @@ def test_entry_points_reject_before_device_work(lib):
     st = lib.kda_verify_f32conv(*args, -5.0, 0.088, 1e-6, P(0x1000), P(0x1000), None, None,
                                 4, 2, 40, 6, 4, 4, 1, 0, -1, None)
     assert st == NUL
+
+
+def test_split_rejects_before_device_work(lib):
+    """The split entry points run the step's checks, then their own: the
+    split factor and the workspace (NULL, too small, misaligned)."""
+    P = ctypes.c_void_p
+    dummy = [P(0x1000)] * 13
+    args = dummy[:2] + [None] + dummy[3:13]
+    assert lib.kda_split_workspace_bytes(4, 2, 1) == 4 * 2 * (1 + 64) * 4
+    assert lib.kda_split_workspace_bytes(4, 2, 8) == 4 * 2 * (1 + 8 * 64) * 4
+    for bad in ((0, 2, 1), (4, 0, 1), (4, 2, 0), (4, 2, 9)):
+        assert lib.kda_split_workspace_bytes(*bad) == 0
+    ws = P(0x2000)
+    need = lib.kda_split_workspace_bytes(4, 2, 1)
+    need4 = lib.kda_split_workspace_bytes(4, 2, 4)
+
+    def dec(gate_mode=0, split=4, w=ws, nbytes=need, W=3):
+        return lib.kda_decode_split(*args, -5.0, 0.088, 1e-6, P(0x1000), 4, 2, 5, W, gate_mode,
+                                    split, w, nbytes, None)
+
+    def ver(T=4, split=2, w=ws, nbytes=need4, W=6, stride=4):
+        return lib.kda_verify_split(*args, -5.0, 0.088, 1e-6, P(0x1000), P(0x1000), 4, 2, 40,
+                                    W, T, stride, 0, split, w, nbytes, None)
+
+    assert dec(gate_mode=2) == GM
+    assert dec(W=2) == SHP
+    for split in (3, 5, 8, -1):
+        assert dec(split=split) == SHP
+    assert dec(w=None) == WSP
+    assert dec(nbytes=need - 1) == WSP
+    assert dec(w=P(0x2002)) == WSP
+    assert ver(split=0, w=None) == WSP            # 8 items, T = 4: the library splits
+    assert ver(T=2, split=2, w=None) == WSP       # an explicit split needs the workspace
+    assert ver(nbytes=need4 - 4) == WSP           # sized for T = 4
+    assert ver(T=1) == TOK and ver(T=9, W=11, stride=9) == TOK
+    assert ver(W=5) == SHP and ver(stride=3) == SHP and ver(split=6) == SHP
+    assert ver(w=None) == WSP and ver(nbytes=0) == WSP
+    # B = 0 is a no-op before the workspace is looked at
+    assert lib.kda_decode_split(*args, -5.0, 0.088, 1e-6, P(0x1000), 0, 2, 5, 3, 0, 4, None, 0,
+                                None) == OK
 
 
 def test_replay_rejects_before_device_work(lib):
