@@ -69,8 +69,11 @@ typedef enum kda_status {
   KDA_ERR_LAUNCH = 6,     /* the kernel launch failed (hipGetLastError) */
   KDA_ERR_ALIGN = 7,      /* a pointer not aligned as its operand needs (see the
                              alignment convention above) */
-  KDA_ERR_WORKSPACE = 8   /* a split call's workspace is NULL, smaller than
+  KDA_ERR_WORKSPACE = 8,  /* a split call's workspace is NULL, smaller than
                              kda_split_workspace_bytes or not 4-byte aligned */
+  KDA_ERR_SCRATCH = 9     /* kda_verify_split_noalloc: the split the call needs
+                             does not fit the library's static scratch
+                             (B*H*(1 + 64*T) 32-bit words above 1024*(1 + 64*8)) */
 } kda_status;
 
 /*
@@ -220,6 +223,32 @@ kda_status kda_verify_split(const uint16_t* x, const uint16_t* conv_w, const uin
                             const uint16_t* f_b, const int32_t* accepted, int B, int H, int N,
                             int W, int T, int slot_stride, int gate_mode, int split,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_verify_split_noalloc -- kda_verify_split for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same operands and results without
+ * the workspace argument.  The workspace is a file-scope device array of the
+ * library, 1024*(1 + 64*8) 32-bit words (2.0 MiB) per GPU, held until the
+ * process ends; its address is looked up (hipGetSymbolAddress) on the first
+ * call made with a given device current, the only set-up, and nothing is
+ * allocated or freed.  A call whose split needs more than the array holds
+ * (B*H*(1 + 64*T) words) returns KDA_ERR_SCRATCH before any device work;
+ * one that runs unsplit (split 1, or the library's choice) needs none and
+ * runs kda_verify.  Every call on one GPU shares that GPU's array: calls that
+ * may run at the same time on one GPU (other streams) race and must not
+ * overlap.  The counters in the array start at zero and every completed
+ * launch leaves them at zero.
+ */
+kda_status kda_verify_split_noalloc(const uint16_t* x, const uint16_t* conv_w,
+                                    const uint16_t* conv_b, uint16_t* conv_state,
+                                    const uint16_t* f_a, const uint16_t* beta, const float* a_log,
+                                    const float* dt_bias, const int32_t* slots, float* state,
+                                    uint16_t* out, const uint16_t* gate, const uint16_t* norm_w,
+                                    float lower_bound, float scale, float eps,
+                                    const uint16_t* f_b, const int32_t* accepted, int B, int H,
+                                    int N, int W, int T, int slot_stride, int gate_mode,
+                                    int split, void* stream);
 
 /*
  * kda_replay -- RecoverSSM: the state after the first n accepted tokens of a

@@ -7,4 +7,5 @@ makes seeded synthetic operands.  Importing the package loads nothing.
 """
 
 from .kda import (kda_decode, kda_decode_split, kda_replay, kda_status_string,  # noqa: F401
-                  kda_validate, kda_verify, kda_verify_split, load_library, split_workspace)
+                  kda_validate, kda_verify, kda_verify_split, kda_verify_split_noalloc,
+                  load_library, split_workspace)

@@ -31,6 +31,8 @@
 // invalidate (acquire) serialise across the device and cost more than the
 // split gains.  Each part repeats the convolution, the gate projection and
 // the decay, which need all 128 channels.
+#include <mutex>
+
 #include "kda.h"
 #include "kda_host.hpp"
 
@@ -300,6 +302,44 @@ kda_status prepare_split(const Args& A, int T, int gate_mode, int split, const v
   return check_split(A, T, split, workspace, workspace_bytes, G);
 }
 
+// ---- the entry point that allocates nothing ---------------------------------
+//
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the split verify with its workspace in a file-scope device array.
+// Each GPU the library runs on holds one copy until the process ends; the
+// host finds that GPU's copy with hipGetSymbolAddress on the first call made
+// with the device current, and passes that address to the kernels (the
+// array's name in host code is only a host-side stand-in).  The counters
+// (the first words) start at zero when the code object is loaded, and every
+// completed launch leaves them at zero.  Every call on a GPU shares that
+// GPU's array: calls that may overlap on one GPU (other streams) race.
+constexpr long long kScratchItems = 1024;
+constexpr size_t kScratchWords = static_cast<size_t>(kScratchItems) * (1 + (kD / 2) * kMaxT);
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // per device, set once
+
+// The current device's copy of `scratch`, or nullptr (status in *err).
+uint32_t* device_scratch(kda_status* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = KDA_ERR_LAUNCH;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *err = KDA_ERR_LAUNCH;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return static_cast<uint32_t*>(g_scratch_ptr[dev]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -351,6 +391,34 @@ kda_status kda_verify_split(const uint16_t* x, const uint16_t* conv_w, const uin
                       H, N, W, T, slot_stride, 0, gate_mode, -1, stream);
   return launch_split(A, T, G, static_cast<uint32_t*>(workspace),
                       static_cast<hipStream_t>(stream));
+}
+
+kda_status kda_verify_split_noalloc(const uint16_t* x, const uint16_t* conv_w,
+                                    const uint16_t* conv_b, uint16_t* conv_state,
+                                    const uint16_t* f_a, const uint16_t* beta, const float* a_log,
+                                    const float* dt_bias, const int32_t* slots, float* state,
+                                    uint16_t* out, const uint16_t* gate, const uint16_t* norm_w,
+                                    float lower_bound, float scale, float eps,
+                                    const uint16_t* f_b, const int32_t* accepted, int B, int H,
+                                    int N, int W, int T, int slot_stride, int gate_mode,
+                                    int split, void* stream) {
+  if (T == 1) return KDA_ERR_TOKENS;
+  const Args A = pack(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state,
+                      out, gate, norm_w, lower_bound, scale, eps, f_b, accepted, nullptr,
+                      nullptr, B, H, N, W, slot_stride, 0);
+  kda_status s = check(A, T, 0, gate_mode);
+  if (s != KDA_OK || B == 0) return s;
+  if (split != 0 && split != 1 && split != 2 && split != 4) return KDA_ERR_SHAPE;
+  const long long items = static_cast<long long>(B) * H;
+  const int G = split == 0 ? auto_split(items, T) : split;
+  if (G == 1)
+    return kda_verify(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
+                      gate, norm_w, lower_bound, scale, eps, f_b, accepted, nullptr, nullptr, B,
+                      H, N, W, T, slot_stride, 0, gate_mode, -1, stream);
+  if (split_bytes(B, H, T) > sizeof(scratch)) return KDA_ERR_SCRATCH;
+  uint32_t* ws = device_scratch(&s);
+  if (!ws) return s;
+  return launch_split(A, T, G, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

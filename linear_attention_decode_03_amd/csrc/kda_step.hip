@@ -521,6 +521,8 @@ const char* kda_status_string(kda_status status) {
     case KDA_ERR_LAUNCH: return "kernel launch failed";
     case KDA_ERR_ALIGN: return "a pointer is not aligned as its operand needs";
     case KDA_ERR_WORKSPACE: return "the split workspace is missing, too small or misaligned";
+    case KDA_ERR_SCRATCH:
+      return "the split needs more than the static scratch holds (B*H*(1 + 64*T) words > 1024*513)";
   }
   return "unknown status";
 }

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 HEAD_DIM = 128
 
 KDA_OK, KDA_ERR_TOKENS, KDA_ERR_GATE_MODE, KDA_ERR_RECORD_T1, KDA_ERR_NULL, KDA_ERR_SHAPE, \
-    KDA_ERR_LAUNCH, KDA_ERR_ALIGN, KDA_ERR_WORKSPACE = range(9)
+    KDA_ERR_LAUNCH, KDA_ERR_ALIGN, KDA_ERR_WORKSPACE, KDA_ERR_SCRATCH = range(10)
 
 _lib = None
 _P = ctypes.c_void_p
@@ -64,6 +64,8 @@ def load_library(path: str = LIB_PATH):
         lib.kda_decode_split.argtypes = _OPERANDS + [_I] * 6 + [_P, ctypes.c_size_t, _P]
         lib.kda_verify_split.restype = _I
         lib.kda_verify_split.argtypes = _OPERANDS + [_P] + [_I] * 8 + [_P, ctypes.c_size_t, _P]
+        lib.kda_verify_split_noalloc.restype = _I
+        lib.kda_verify_split_noalloc.argtypes = _OPERANDS + [_P] + [_I] * 8 + [_P]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [_I]
         _lib = lib
@@ -296,6 +298,37 @@ def kda_verify_split(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, s
             _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
             _ptr(accepted), B, H, N, W, T, int(slots.shape[1]), int(gate_mode), int(split),
             ws, ws_bytes, _stream(stream, state.device))
+    _raise(status)
+
+
+def kda_verify_split_noalloc(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots,
+                             state, out, gate, norm_w, lower_bound, scale, eps, f_b, accepted,
+                             T=None, split=0, gate_mode=0, stream=None):
+    """kda_verify_split with the library's static scratch instead of a
+    workspace: allocates nothing (see kda_verify_split_noalloc in
+    include/kda.h; calls that may overlap on one GPU race)."""
+    import torch
+
+    if slots.dim() != 2:
+        raise ValueError("slots: expected [B, slot_stride]")
+    T = int(T if T is not None else slots.shape[1])
+    if not 1 <= T <= 8:
+        _raise(KDA_ERR_TOKENS)
+    B, H, N, W = _sizes(x, state, conv_state, T)
+    _check_common(x, conv_w, conv_b, conv_state, f_a, beta, a_log, dt_bias, slots, state, out,
+                  gate, norm_w, f_b, B, H, T)
+    if conv_state.dtype != torch.bfloat16:
+        raise ValueError("conv_state: the split step takes a BF16 convolution pool")
+    _check("accepted", accepted, torch.int32, 1, state.device)
+    if accepted.shape[0] != B:
+        raise ValueError("accepted: expected [B]")
+    with torch.cuda.device(state.device):
+        status = load_library().kda_verify_split_noalloc(
+            _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(f_a), _ptr(beta),
+            _ptr(a_log), _ptr(dt_bias), _ptr(slots), _ptr(state), _ptr(out), _ptr(gate),
+            _ptr(norm_w), float(lower_bound), float(scale), float(eps), _ptr(f_b),
+            _ptr(accepted), B, H, N, W, T, int(slots.shape[1]), int(gate_mode), int(split),
+            _stream(stream, state.device))
     _raise(status)
 
 

@@ -36,19 +36,20 @@ def test_exports_every_declared_symbol(lib):
     names = declared()
     assert names == ["kda_decode", "kda_decode_f32conv", "kda_decode_split", "kda_replay",
                      "kda_split_workspace_bytes", "kda_status_string", "kda_validate",
-                     "kda_verify", "kda_verify_f32conv", "kda_verify_split"]
+                     "kda_verify", "kda_verify_f32conv", "kda_verify_split",
+                     "kda_verify_split_noalloc"]
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = kda.kda_status_string(code)
         assert s and s != "unknown status"
     assert kda.kda_status_string(99) == "unknown status"
 
 
-OK, TOK, GM, REC, NUL, SHP, ALN, WSP = 0, 1, 2, 3, 4, 5, 7, 8
+OK, TOK, GM, REC, NUL, SHP, ALN, WSP, SCR = 0, 1, 2, 3, 4, 5, 7, 8, 9
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -166,6 +167,16 @@ def test_split_rejects_before_device_work(lib):
     assert ver(T=1) == TOK and ver(T=9, W=11, stride=9) == TOK
     assert ver(W=5) == SHP and ver(stride=3) == SHP and ver(split=6) == SHP
     assert ver(w=None) == WSP and ver(nbytes=0) == WSP
+    # the entry point without a workspace: the same checks, then the size of
+    # the static scratch (1024 items at T = 8), all before any HIP call
+    def noalloc(B=4, H=2, T=4, split=4, W=6, stride=4):
+        return lib.kda_verify_split_noalloc(*args, -5.0, 0.088, 1e-6, P(0x1000), P(0x1000), B, H,
+                                            40, W, T, stride, 0, split, None)
+
+    assert noalloc(T=1) == TOK and noalloc(split=3) == SHP and noalloc(W=5) == SHP
+    assert noalloc(B=64, H=32, T=4, split=4) == SCR      # 2048 items
+    assert noalloc(B=33, H=32, T=8, split=2, W=10, stride=8) == SCR   # 1056 items
+    assert noalloc(B=0) == OK
     # B = 0 is a no-op before the workspace is looked at
     assert lib.kda_decode_split(*args, -5.0, 0.088, 1e-6, P(0x1000), 0, 2, 5, 3, 0, 4, None, 0,
                                 None) == OK
