@@ -596,7 +596,7 @@ __device__ __forceinline__ void gate_rounds_compute(GateRounds<T>& gr, SH& sh) {
 // The record kernel's variant: the f_a rows of the item are converted to
 // FP64 once, into an LDS table shared by the four waves, so the B operand
 // of every gate step is one 8-byte LDS read instead of a global load and
-// two conversions per lane; only the F_B rows come in rounds.  Column
+// two conversions per lane; the F_B rows stay in registers.  Column
 // 32k + r of token t sits at t * kFaPitch + 33k + r (doubles): the 16
 // distinct addresses of one read (4 tokens x 4 column quarters) fall in
 // distinct banks.
@@ -637,28 +637,33 @@ __device__ __forceinline__ void fa_pairs_store(const FaPairs<T>& fp, double* fa6
   }
 }
 
+// All four column rounds of the F_B rows at once, loaded with the other
+// input operands so that the gate waits on no memory (a load issued after
+// the state page would retire after it).
 template <int T>
-struct GateRoundsFB {
-  const uint16_t* fb_base;  // wave-uniform
-  uint32_t fb_off;          // lane offset in elements
-  uint4 fb[2];              // the current round
+struct GateFBAll {
+  uint4 fb[4][2];  // [column step n][feature group fg]
 };
 
 template <int T>
-__device__ __forceinline__ void gate_fb_rounds_begin(const Args& A, const Item& it,
-                                                     GateRoundsFB<T>& gr) {
+__device__ __forceinline__ void gate_fb_all_load(const Args& A, const Item& it, GateFBAll<T>& gf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int k = lane >> 4, b = (lane >> 2) & 3, i = lane & 3;
-  gr.fb_base = A.f_b + static_cast<size_t>(it.h) * kD * kD;
-  gr.fb_off = (32 * wave + 4 * b + i) * kD + 32 * k;  // feature group 1: 16 rows on
+  const uint16_t* base = A.f_b + static_cast<size_t>(it.h) * kD * kD +
+                         (32 * wave + 4 * b + i) * kD + 32 * k;
 #pragma unroll
-  for (int fg = 0; fg < 2; ++fg)
-    gr.fb[fg] = *reinterpret_cast<const uint4*>(gr.fb_base + gr.fb_off + 16 * kD * fg);
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int fg = 0; fg < 2; ++fg)
+      gf.fb[n][fg] = *reinterpret_cast<const uint4*>(base + 16 * kD * fg + 8 * n);
 }
 
+// The 4x4x4 FP64 projection (the lane layout of gate_quad_compute) with F_B
+// in registers and f_a from the FP64 table in LDS: each B operand is one
+// 8-byte LDS read.
 template <int T, class SH>
-__device__ __forceinline__ void gate_fb_rounds_compute(GateRoundsFB<T>& gr, const double* fa64,
-                                                       SH& sh) {
+__device__ __forceinline__ void gate_fb_all_compute(const GateFBAll<T>& gf, const double* fa64,
+                                                    SH& sh) {
   constexpr int kTG = GateQuadOperands<T>::kTokenGroups;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int k = lane >> 4, b = (lane >> 2) & 3, j = lane & 3;
@@ -673,13 +678,8 @@ __device__ __forceinline__ void gate_fb_rounds_compute(GateRoundsFB<T>& gr, cons
   for (int fg = 0; fg < 2; ++fg)
 #pragma unroll
     for (int tg = 0; tg < kTG; ++tg) acc[fg][tg] = 0.0;
-#pragma unroll 1
-  for (int n = 0; n < 4; ++n) {
-    const uint32_t col = 8 * (n < 3 ? n + 1 : n);
-    uint4 fb_next[2];
 #pragma unroll
-    for (int fg = 0; fg < 2; ++fg)
-      fb_next[fg] = *reinterpret_cast<const uint4*>(gr.fb_base + gr.fb_off + 16 * kD * fg + col);
+  for (int n = 0; n < 4; ++n)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       double bv[kTG];
@@ -687,15 +687,12 @@ __device__ __forceinline__ void gate_fb_rounds_compute(GateRoundsFB<T>& gr, cons
       for (int tg = 0; tg < kTG; ++tg) bv[tg] = fa64[row[tg] + 8 * n + e];
 #pragma unroll
       for (int fg = 0; fg < 2; ++fg) {
-        const double av = static_cast<double>(bf16_at(gr.fb[fg], e));
+        const double av = static_cast<double>(bf16_at(gf.fb[n][fg], e));
 #pragma unroll
         for (int tg = 0; tg < kTG; ++tg)
           acc[fg][tg] = __builtin_amdgcn_mfma_f64_4x4x4f64(av, bv[tg], acc[fg][tg], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int fg = 0; fg < 2; ++fg) gr.fb[fg] = fb_next[fg];
-  }
 #pragma unroll
   for (int fg = 0; fg < 2; ++fg) {
     const int f = 32 * wave + 16 * fg + 4 * b + (lane >> 4);

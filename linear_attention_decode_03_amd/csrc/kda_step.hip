@@ -207,19 +207,22 @@ void kda_step_latency_kernel(const Args A) {
 // 16q + 4g + [0, 4)).  Used when |lower_bound| <= 10, so that every A_t and
 // 1 / A_t stays a normal FP32 number (|log A_t| <= 80).
 template <int T, bool kBias, bool kConvF32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void kda_record_kernel(const Args A) {
-  // 1. The input operands ahead of the state page (loads of a wave retire in
+  // 1. Every input operand ahead of the state page (loads of a wave retire in
   //    issue order, so nothing that the prologue needs may queue behind the
-  //    page): convolution inputs, gate rows, f_a, beta, dt_bias before the
-  //    slot tables are read, the window taps after; the output-norm operands
-  //    after the gate.  The scheduling barriers keep the groups in this order.
+  //    page): convolution inputs, all F_B rows of the gate, f_a, beta,
+  //    dt_bias before the slot tables are read, the window taps after.  The
+  //    page's first row tile is issued right after the taps and arrives
+  //    during the convolution and the gate; the second after the gate,
+  //    behind the output-norm operands.  The scheduling barriers keep the
+  //    groups in this order.
   Item it;
   locate<T>(A, it);
   ConvOperands<T> co;
   conv_load_inputs<T, kBias>(A, it, co);
-  GateRoundsFB<T> gr;
-  gate_fb_rounds_begin<T>(A, it, gr);
+  GateFBAll<T> gf;
+  gate_fb_all_load<T>(A, it, gf);
   FaPairs<T> fp;
   fa_pairs_load<T>(A, it, fp);
   const float beta_logit = load_beta<T>(A, it);
@@ -236,6 +239,14 @@ void kda_record_kernel(const Args A) {
   const int g = lane >> 4, c = lane & 15;
   conv_load_taps<T, kConvF32>(A, it, co);
   __builtin_amdgcn_sched_barrier(0);
+  // S0 in the MFMA B-operand layout: [tile][q] = rows 32w + 16 tile + c,
+  // keys 16q + 4g .. +3 (each instruction: 16 rows x 64 contiguous bytes).
+  float4 st[2][8];
+  const __amdgpu_buffer_rsrc_t page = page_rsrc(A.state, it.rs, it.h, A.H);
+  const int voff = (32 * wave + c) * kD * 4 + 16 * g;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) st[0][q] = load_f4(page, voff, 64 * q);
+  __builtin_amdgcn_sched_barrier(0);
   // f_a in FP64 for the gate, in the space of W (written only in step 4)
   static_assert(T * kFaPitch * sizeof(double) <= sizeof(rt.W), "f_a table exceeds W");
   double* fa64 = reinterpret_cast<double*>(&rt.W[0][0]);
@@ -245,24 +256,15 @@ void kda_record_kernel(const Args A) {
   // 2. Convolution, norms, gate projection.
   conv_compute<T, true, kConvF32>(A, it, sh, co);
   store_beta<T>(sh, beta_logit);
-  gate_fb_rounds_compute<T>(gr, fa64, sh);
+  gate_fb_all_compute<T>(gf, fa64, sh);
   OutputOperands<T> oo;
   load_output_operands<T>(A, it, oo);
   __syncthreads();
 
-  // 3. S0 into the MFMA B-operand layout: [tile][q] = rows 32w + 16 tile + c,
-  //    keys 16q + 4g .. +3 (each instruction: 16 rows x 64 contiguous bytes).
-  //    Issued once the gate operands are dead; the decay and the W and X
-  //    tables are computed while it arrives.
-  float4 st[2][8];
-  {
-    const __amdgpu_buffer_rsrc_t page = page_rsrc(A.state, it.rs, it.h, A.H);
-    const int voff = (32 * wave + c) * kD * 4 + 16 * g;
+  // 3. The page's second row tile; the decay and the W and X tables are
+  //    computed while it arrives.
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) st[tile][q] = load_f4(page, voff, tile * 16 * kD * 4 + 64 * q);
-  }
+  for (int q = 0; q < 8; ++q) st[1][q] = load_f4(page, voff, 16 * kD * 4 + 64 * q);
   float sink;
   prefetch_page<T>(A, sink);
   decay<T, true>(A, it, sh, dt);
