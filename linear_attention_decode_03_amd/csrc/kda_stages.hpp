@@ -722,6 +722,46 @@ __device__ __forceinline__ void decay(const Args& A, const Item& it, SH& sh, flo
   }
 }
 
+// Token halves for the per-channel stages of the record kernel: thread tid
+// takes channel tid & 127 and, in step j < kHalfTokens, token
+// half_token<T>(j) of its half (tid >> 7: the first (T + 1) / 2 tokens, or
+// the rest), so all four waves share the work that threads 0-127 would do
+// alone.  Each value is computed by the same operations as with one thread
+// per channel, so the results are the same bits.  Steps and register
+// indices stay compile-time constants (a select by the wave-uniform half).
+template <int T>
+constexpr int kHalfTokens = (T + 1) / 2;
+
+__device__ __forceinline__ bool second_half() { return (threadIdx.x >> 7) != 0; }
+
+template <int T>
+__device__ __forceinline__ int half_token(int j) {
+  return second_half() ? kHalfTokens<T> + j : j;
+}
+
+// Step j exists in both halves, or only in the first (odd T).
+template <int T>
+__device__ __forceinline__ bool half_step_live(int j) {
+  return !second_half() || kHalfTokens<T> + j < T;
+}
+
+// The decay (and the record of raw_g) of decay<T, true>, by token halves.
+template <int T, class SH>
+__device__ __forceinline__ void decay_halves(const Args& A, const Item& it, SH& sh, float dt) {
+  const int f = threadIdx.x & (kD - 1);
+  const float e = expf(A.a_log[it.h]);
+#pragma unroll
+  for (int j = 0; j < kHalfTokens<T>; ++j) {
+    if (half_step_live<T>(j)) {
+      const int t = half_token<T>(j);
+      const float raw_g = round_bf16(sh.u.in.g[t][f]);
+      sh.u.in.a[t][f] = decay_f32(e, raw_g, dt, A.lower_bound);
+      A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + kD + f] =
+          static_cast<uint16_t>(f32_to_bf16_bits(raw_g));
+    }
+  }
+}
+
 // dt_bias of key channel tid (threads 0-127), loaded with the input operands.
 __device__ __forceinline__ float load_dt(const Args& A, const Item& it) {
   return A.dt_bias[static_cast<size_t>(it.h) * kD + (threadIdx.x & (kD - 1))];
@@ -760,6 +800,39 @@ __device__ __forceinline__ void gated_rmsnorm(const Args& A, const Item& it, SH&
       const float sg = sigmoid_fast(bf16_bits_to_f32(oo.gate[t]));
       const size_t idx = (it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + tid;
       A.out[idx] = static_cast<uint16_t>(f32_to_bf16_bits(((o[t][tid] * rstd) * oo.nw) * sg));
+    }
+  }
+}
+
+// The gated RMSNorm of gated_rmsnorm by token halves: waves 0-1 take the
+// first half of the tokens, waves 2-3 the second, each pair summing o^2
+// over the 128 channels (64 per wave) in the same order.
+template <int T, class SH>
+__device__ __forceinline__ void gated_rmsnorm_halves(const Args& A, const Item& it, SH& sh,
+                                                     const float (*o)[kD],
+                                                     const OutputOperands<T>& oo) {
+  const int tid = threadIdx.x, lane = tid & 63, pw = (tid >> 6) & 1;
+  const int c = tid & (kD - 1);
+#pragma unroll
+  for (int j = 0; j < kHalfTokens<T>; ++j) {
+    if (half_step_live<T>(j)) {
+      const float ot = o[half_token<T>(j)][c];
+      const float ss = wave_sum(ot * ot);
+      if (lane == 0) sh.os[half_token<T>(j)][pw] = ss;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kHalfTokens<T>; ++j) {
+    if (half_step_live<T>(j)) {
+      const int t = half_token<T>(j);
+      const int kHi = kHalfTokens<T> + j < T ? kHalfTokens<T> + j : j;  // constant once unrolled
+      const uint32_t gbits = second_half() ? oo.gate[kHi] : oo.gate[j];
+      const float variance = (sh.os[t][0] + sh.os[t][1]) * (1.0f / 128.0f) + A.eps;
+      const float rstd = __builtin_amdgcn_rsqf(variance);
+      const float sg = sigmoid_fast(bf16_bits_to_f32(gbits));
+      const size_t idx = (it.token0 + t) * it.dim + static_cast<size_t>(it.h) * kD + c;
+      A.out[idx] = static_cast<uint16_t>(f32_to_bf16_bits(((o[t][c] * rstd) * oo.nw) * sg));
     }
   }
 }

@@ -267,28 +267,39 @@ void kda_record_kernel(const Args A) {
   for (int q = 0; q < 8; ++q) st[1][q] = load_f4(page, voff, 16 * kD * 4 + 64 * q);
   float sink;
   prefetch_page<T>(A, sink);
-  decay<T, true>(A, it, sh, dt);
+  decay_halves<T>(A, it, sh, dt);
   __syncthreads();
 
-  // 4. W and X (thread = key channel), W zero beyond row 2T.  X takes the
-  //    space of the FP32 gate projection, dead since the decay.
+  // 4. W and X (thread = key channel, token half), W zero beyond row 2T.  X
+  //    takes the space of the FP32 gate projection, dead since the decay.
+  //    The second half first forms the running product over the first
+  //    half's tokens itself, with the same multiplications in order.
   float (&X)[T][kPad] = sh.u.in.g;
-  if (tid < kD) {
-    const int key = tid;
+  {
+    const int key = tid & (kD - 1);
     float acc = 1.0f;
+    if (second_half()) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float fq, fk;
-      norm_factors<T>(sh, t, fq, fk);
-      acc = acc * sh.u.in.a[t][key];
-      const float kh = sh.u.in.k[t][key] * fk;
-      const float qh = (sh.u.in.q[t][key] * fq) * A.scale;
-      rt.W[t][key] = acc * kh;
-      rt.W[T + t][key] = acc * qh;
-      X[t][key] = kh * __builtin_amdgcn_rcpf(acc);  // acc a normal number (bound above)
+      for (int t = 0; t < kHalfTokens<T>; ++t) acc = acc * sh.u.in.a[t][key];
     }
 #pragma unroll
-    for (int m = 2 * T; m < 16; ++m) rt.W[m][key] = 0.0f;
+    for (int j = 0; j < kHalfTokens<T>; ++j) {
+      if (half_step_live<T>(j)) {
+        const int t = half_token<T>(j);
+        float fq, fk;
+        norm_factors<T>(sh, t, fq, fk);
+        acc = acc * sh.u.in.a[t][key];
+        const float kh = sh.u.in.k[t][key] * fk;
+        const float qh = (sh.u.in.q[t][key] * fq) * A.scale;
+        rt.W[t][key] = acc * kh;
+        rt.W[T + t][key] = acc * qh;
+        X[t][key] = kh * __builtin_amdgcn_rcpf(acc);  // acc a normal number (bound above)
+      }
+    }
+    if (tid >= kD) {
+#pragma unroll
+      for (int m = 2 * T; m < 16; ++m) rt.W[m][key] = 0.0f;
+    }
   }
   __syncthreads();  // from here q, k, a and g are dead: P, C and o take their space
 
@@ -353,8 +364,8 @@ void kda_record_kernel(const Args A) {
   }
   __syncthreads();
 
-  // 7. Gated RMSNorm.
-  gated_rmsnorm<T>(A, it, sh, sh.u.out.o, oo);
+  // 7. Gated RMSNorm (token halves over the four waves).
+  gated_rmsnorm_halves<T>(A, it, sh, sh.u.out.o, oo);
   keep_alive(A, sink);
 }
 
