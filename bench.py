@@ -6,22 +6,25 @@ gated RMSNorm) over one batch: the decode workload B=256 requests x H=32
 heads (8192 items), T=1, d=128, a pool of 512 state slots (1 GiB FP32), with
 seeded synthetic inputs resident in HBM before the timed region.
 
-Prints one JSON line.  `value` is (request, head) items per second;
-`roofline` relates the kernel's algorithmic bytes per launch to its average
-duration: the span of one pair of HIP events on the launch stream around the
-K back-to-back launches of the timed region, divided by K
-(`single_launch_us` gives the spread of launches timed one by one in a
-second pass); `roofline.cold` times launches each preceded by a 1 GiB
-scratch write, so that no operand is cached (and the caches hold dirty
-lines), `roofline.cold_clean` with a 1 GiB read instead;
-`roofline.copy_ceiling` is what a plain 1 GiB device copy reaches on the
-same GPU;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Prints one JSON line.  `value` is (request, head) items per second over the
+timed region.  `roofline` relates the kernel's algorithmic bytes per launch
+to its duration.  The headline (`achieved`, `frac`, `kernel_us`) is the
+cold-clean median: launches each preceded by a 1 GiB read, so that no
+operand is cached.  Secondary figures:
+  * `roofline.warm`: the span of one pair of HIP events on the launch
+    stream around the K back-to-back launches of the timed region, / K;
+  * `roofline.cold_dirty`: launches each after a 1 GiB write (dirty lines
+    written back during the launch);
+  * `single_launch_us`: launches timed one by one;
+  * `roofline.copy_ceiling`: what a plain 1 GiB device copy reaches.
+`cpu_baseline` times the CPU oracle on the same workload, pinned to one core
+(the median over whole passes), and split over host threads.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                     [--cold-launches C]
     python bench.py --mode copy      # 1 GiB device copies (counter calibration)
     python bench.py --mode sweep     # small batches, unsplit vs split (graph replay)
+    python bench.py --mode pagecopy [--workload W]   # the page traffic alone (its ceiling)
 
 Workloads: tiny_decode, decode_b64, decode_b256 (default), verify_t4,
 verify_record_t8 (the step), and replay_t8 (the RecoverSSM replay of
@@ -119,29 +122,35 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(p, replay=False, min_seconds=10.0):
-    """The oracle as it is (single-threaded C) on the same workload: whole
-    passes over all items (the step, or the replay) until at least
-    `min_seconds` have elapsed."""
+def cpu_baseline(p, replay=False, min_seconds=10.0, min_passes=3):
+    """The oracle as it is (single-threaded C) on the same workload, with this
+    process pinned to one core while it runs: whole passes over all items
+    (the step, or the replay), at least `min_passes` and until `min_seconds`
+    have elapsed; the rate is the median over the passes."""
     import oracle
     from linear_attention_decode_03_amd.inputs import copy_problem
 
     oracle.build(force=False)
     q = copy_problem(p)
     n_items = p["B"] * p["H"]
-    done, t0 = 0, time.perf_counter()
-    while True:
-        if replay:
-            oracle.replay(q)
-        else:
-            oracle.run(q)
-        done += n_items
+    cores = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {cores[0]})
+    try:
+        rates, t0 = [], time.perf_counter()
+        while len(rates) < min_passes or time.perf_counter() - t0 < min_seconds:
+            ts = time.perf_counter()
+            if replay:
+                oracle.replay(q)
+            else:
+                oracle.run(q)
+            rates.append(n_items / (time.perf_counter() - ts))
         el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    res = {"value": done / el, "unit": "items/s", "cores": 1, "kind": "oracle",
-           "sample": f"{done // n_items} full pass(es) over the {n_items} items of the "
-                     f"same workload, single-threaded, {el:.1f} s",
+    finally:
+        os.sched_setaffinity(0, set(cores))
+    rates.sort()
+    res = {"value": rates[len(rates) // 2], "unit": "items/s", "cores": 1, "kind": "oracle",
+           "sample": f"median of {len(rates)} full passes over the {n_items} items of the same "
+                     f"workload, single-threaded, pinned to core {cores[0]}, {el:.1f} s",
            "cpu_model": cpu_model()}
     if not replay:
         res["threaded"] = cpu_baseline_threaded(q, min_seconds=min_seconds / 2)
@@ -149,13 +158,21 @@ def cpu_baseline(p, replay=False, min_seconds=10.0):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it (model name, family, model and
+    the number of logical CPUs)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                fields.setdefault(k, v)
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if not name:
+        return None
+    return (f"{name} (family {fields.get('cpu family', '?')}, model {fields.get('model', '?')}; "
+            f"{os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} usable)")
 
 
 def cpu_baseline_threaded(q, min_seconds=5.0, max_threads=16):
@@ -291,6 +308,69 @@ def run_sweep(args):
             print(json.dumps(row), flush=True)
 
 
+def run_pagecopy(args):
+    """The ceiling of the step's page traffic: kda_page_copy on the workload's
+    own slot tables (each item reads its 64 KiB page and writes it to its
+    stored-token targets: in place for decode, T pages for verify, none for
+    record), in the step kernels' access shape and with no compute.  Times K
+    back-to-back launches between one event pair, and cold-clean launches
+    (each after a 1 GiB read); prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from linear_attention_decode_03_amd import device as dev
+    from linear_attention_decode_03_amd import inputs, kda
+
+    kda.load_library()
+    p = inputs.make_problem(args.workload)
+    B, T = p["B"], p["T"]
+    if T == 1:
+        src = p["slots"].astype(np.int32)
+        dst = src.reshape(B, 1).copy()
+    else:
+        src = p["slots"][np.arange(B), p["accepted"] - 1].astype(np.int32)
+        dst = p["slots"][:, :T].copy() if not p["record"] else np.zeros((B, 0), np.int32)
+    n_dst = dst.shape[1]
+    d = dev.to_device(p)
+    src_t = torch.from_numpy(np.ascontiguousarray(src)).cuda()
+    dst_t = torch.from_numpy(np.ascontiguousarray(dst)).cuda() if n_dst else None
+
+    def step():
+        kda.kda_page_copy(d["state"], src_t, dst_t, n_dst)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1e3 / K
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flush.fill_(1.0)
+    clean = []
+    for _ in range(max(1, args.cold_launches)):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        clean.append(a.elapsed_time(b) * 1e3)
+    clean.sort()
+    live = int((src > 0).sum()) * p["H"]
+    writes = int((dst > 0).sum()) * p["H"]
+    page_bytes = (live + writes) * 65536
+    print(json.dumps({"mode": "pagecopy", "workload": args.workload, "items": B * p["H"],
+                      "pages_read": live, "pages_written": writes, "bytes": page_bytes,
+                      "warm_us": warm_us, "warm_gbps": page_bytes / warm_us / 1e3,
+                      "clean_us": clean[len(clean) // 2],
+                      "clean_gbps": page_bytes / clean[len(clean) // 2] / 1e3}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,7 +382,7 @@ def main():
     ap.add_argument("--cold-launches", type=int, default=20)
     ap.add_argument("--conv-f32", action="store_true",
                     help="keep the convolution pool in FP32 (kda_*_f32conv)")
-    ap.add_argument("--mode", choices=["kda", "copy", "sweep"], default="kda")
+    ap.add_argument("--mode", choices=["kda", "copy", "sweep", "pagecopy"], default="kda")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -316,6 +396,8 @@ def main():
         return run_copy(args)
     if args.mode == "sweep":
         return run_sweep(args)
+    if args.mode == "pagecopy":
+        return run_pagecopy(args)
 
     from linear_attention_decode_03_amd import device as _gpu
     from linear_attention_decode_03_amd import inputs, kda
@@ -400,8 +482,33 @@ def main():
 
     items = p["B"] * p["H"]
     abytes = replay_algorithmic_bytes(p) if replay else algorithmic_bytes(p)
-    achieved = abytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
+
+    def rate(us):
+        gbps = abytes / (us * 1e-6) / 1e9
+        return {"kernel_us": us, "achieved": gbps, "frac": gbps / HBM_PEAK_GBPS}
+
+    warm = dict(rate(kernel_ms * 1e3), method=f"span of the {K} back-to-back launches of the "
+                "timed region between one event pair on the launch stream, / K")
+    cold_dirty = None if not cold else dict(
+        rate(cold[k_cold // 2] * 1e3), launches=k_cold,
+        method="median of launches each preceded by a 1 GiB write outside its events "
+               "(the caches hold dirty lines written back during the launch)")
+    cold_clean = None if not clean else dict(
+        rate(clean[k_cold // 2] * 1e3), launches=k_cold,
+        method="median of launches each preceded by a 1 GiB read outside its events "
+               "(nothing of the launch is cached, nothing else dirty)")
+    # The headline: cold-clean (no operand cached), else the warm figure.
+    head = cold_clean or warm
+    roofline = {"bound": "hbm", "achieved": head["achieved"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": head["frac"], "kernel_us": head["kernel_us"],
+                "method": "cold_clean" if cold_clean else "warm",
+                "traffic": traffic, "algorithmic_bytes_per_launch": abytes,
+                "warm": warm, "cold_clean": cold_clean, "cold_dirty": cold_dirty,
+                "single_launch_us": {"p10": single[K // 10] * 1e3,
+                                     "median": single[K // 2] * 1e3,
+                                     "p90": single[(9 * K) // 10] * 1e3},
+                "copy_ceiling": copy}
     if not replay:
         extra = {"record": p["record"], "gate_mode": p["gate_mode"],
                  "conv_pool": "f32" if p["conv_f32"] else "bf16"}
@@ -424,24 +531,7 @@ def main():
                                f"T={p['T']}, B={p['B']} requests, H={p['H']} heads, d=128, "
                                f"{p['N']}-slot FP32 state pool",
                    "B": p["B"], "H": p["H"], "T": p["T"], "N": p["N"], "items": items},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": abytes,
-                     "kernel_us": kernel_ms * 1e3,
-                     "single_launch_us": {"p10": single[K // 10] * 1e3,
-                                          "median": single[K // 2] * 1e3,
-                                          "p90": single[(9 * K) // 10] * 1e3},
-                     "cold": None if not cold else {
-                         "kernel_us_median": cold[k_cold // 2] * 1e3, "launches": k_cold,
-                         "achieved": abytes / (cold[k_cold // 2] * 1e-3) / 1e9,
-                         "frac": abytes / (cold[k_cold // 2] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                         "evicted_by": "1 GiB write (dirty lines written back during the launch)"},
-                     "cold_clean": None if not clean else {
-                         "kernel_us_median": clean[k_cold // 2] * 1e3, "launches": k_cold,
-                         "achieved": abytes / (clean[k_cold // 2] * 1e-3) / 1e9,
-                         "frac": abytes / (clean[k_cold // 2] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                         "evicted_by": "1 GiB read"},
-                     "copy_ceiling": copy},
+        "roofline": roofline,
     }
     result["config"].update(extra)
     if not args.no_cpu:

@@ -282,6 +282,24 @@ kda_status kda_replay(const float* rec_u, const uint16_t* rec_kg, const float* a
                       int N, int T, void* stream);
 
 /*
+ * kda_page_copy -- a measurement aid, not a step of the method: the state-page
+ * traffic of the step (the kernel body's one read of an item's 64 KiB page
+ * and one write per stored token) without the compute, in the step kernels'
+ * access shape, to measure what that traffic alone reaches on the GPU.  For
+ * every (request b, head h): read page state[src_slots[b], h] and write it
+ * unchanged to state[dst_slots[b*n_dst + w], h] for w < n_dst (n_dst = 1:
+ * the decode pattern, in place when dst = src; n_dst = T: the verify
+ * pattern; 0: reads only).  A src slot outside [1, N) skips the request, a
+ * dst slot outside [1, N) skips that write.  Caller contract: the dst pages
+ * are distinct across requests and no dst is another request's src.
+ * Status: KDA_ERR_SHAPE (B < 0, H < 1, N < 1, n_dst outside [0, 8], grid
+ * beyond 32 bits), KDA_ERR_NULL, KDA_ERR_ALIGN (state on 16 bytes, tables on
+ * 4), KDA_ERR_LAUNCH; B = 0 is a no-op.
+ */
+kda_status kda_page_copy(float* state, const int32_t* src_slots, const int32_t* dst_slots,
+                         int n_dst, int B, int H, int N, void* stream);
+
+/*
  * kda_validate -- the host-side checks of kda_verify (T = 1 checks a decode
  * call, with slot_stride and accepted ignored) without enqueuing anything.
  * Touches no device memory and makes no HIP call: usable without a GPU.

@@ -2,7 +2,8 @@
 
 The library is built by one hipcc call from the kernel sources in csrc/
 (kda_step.hip: decode, verify and record mode; kda_split.hip: the split
-variant for small batches; kda_replay.hip: the replay; the headers
+variant for small batches; kda_replay.hip: the replay; kda_probe.hip: the
+page-traffic measurement aid; the headers
 kda_device.hpp and kda_stages.hpp hold the shared device code, kda_host.hpp
 the shared host-side checks).
 Packed FP32 instructions are switched off (-packed-fp32-ops): the kernels
@@ -17,7 +18,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("kda_step.hip", "kda_split.hip", "kda_replay.hip")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("kda_step.hip", "kda_split.hip", "kda_replay.hip", "kda_probe.hip")]
 LIB = os.path.join(HERE, "libkda.so")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH):
         lib.kda_verify_split.argtypes = _OPERANDS + [_P] + [_I] * 8 + [_P, ctypes.c_size_t, _P]
         lib.kda_verify_split_noalloc.restype = _I
         lib.kda_verify_split_noalloc.argtypes = _OPERANDS + [_P] + [_I] * 8 + [_P]
+        lib.kda_page_copy.restype = _I
+        lib.kda_page_copy.argtypes = [_P] * 3 + [_I] * 4 + [_P]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [_I]
         _lib = lib
@@ -364,6 +366,26 @@ def kda_replay(rec_u, rec_kg, a_log, dt_bias, src_slots, dst_slots, n_tokens, st
             _ptr(rec_u), _ptr(rec_kg), _ptr(a_log), _ptr(dt_bias), _ptr(src_slots),
             _ptr(dst_slots), _ptr(n_tokens), _ptr(state), float(lower_bound), B, H,
             int(state.shape[0]), T, _stream(stream, dev))
+    _raise(status)
+
+
+def kda_page_copy(state, src_slots, dst_slots, n_dst, stream=None):
+    """A measurement aid: the step's state-page reads and writes without the
+    compute (see kda_page_copy in include/kda.h).  src_slots [B], dst_slots
+    [B, n_dst] int32 on the GPU of `state`."""
+    import torch
+
+    dev = _gpu_device(state)
+    _check("state", state, torch.float32, 4, dev)
+    _check("src_slots", src_slots, torch.int32, 1, dev)
+    B, H, N = int(src_slots.shape[0]), int(state.shape[1]), int(state.shape[0])
+    if n_dst:
+        _check("dst_slots", dst_slots, torch.int32, 2, dev)
+        if tuple(dst_slots.shape) != (B, n_dst):
+            raise ValueError("dst_slots: expected [B, n_dst]")
+    with torch.cuda.device(dev):
+        status = load_library().kda_page_copy(_ptr(state), _ptr(src_slots), _ptr(dst_slots),
+                                              int(n_dst), B, H, N, _stream(stream, dev))
     _raise(status)
 
 

@@ -34,7 +34,8 @@ def declared():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert names == ["kda_decode", "kda_decode_f32conv", "kda_decode_split", "kda_replay",
+    assert names == ["kda_decode", "kda_decode_f32conv", "kda_decode_split", "kda_page_copy",
+                     "kda_replay",
                      "kda_split_workspace_bytes", "kda_status_string", "kda_validate",
                      "kda_verify", "kda_verify_f32conv", "kda_verify_split",
                      "kda_verify_split_noalloc"]
@@ -180,6 +181,17 @@ def test_split_rejects_before_device_work(lib):
     # B = 0 is a no-op before the workspace is looked at
     assert lib.kda_decode_split(*args, -5.0, 0.088, 1e-6, P(0x1000), 0, 2, 5, 3, 0, 4, None, 0,
                                 None) == OK
+
+
+def test_page_copy_rejects_before_device_work(lib):
+    P = ctypes.c_void_p
+    s, src, dst = P(0x1000), P(0x2000), P(0x3000)
+    for args, want in (((s, src, dst, 1, -1, 2, 9), SHP), ((s, src, dst, 9, 4, 2, 9), SHP),
+                       ((s, src, dst, 1, 4, 0, 9), SHP), ((s, src, dst, 1, 0, 2, 9), OK),
+                       ((None, src, dst, 1, 4, 2, 9), NUL), ((s, src, None, 1, 4, 2, 9), NUL),
+                       ((P(0x1008), src, dst, 1, 4, 2, 9), ALN),
+                       ((s, P(0x2002), dst, 1, 4, 2, 9), ALN)):
+        assert lib.kda_page_copy(*args, None) == want, args
 
 
 def test_replay_rejects_before_device_work(lib):
