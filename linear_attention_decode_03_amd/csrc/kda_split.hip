@@ -77,6 +77,7 @@ void kda_split_kernel(const Args A, uint32_t* ws) {
   }
   const float beta_logit = load_beta<T>(A, it);
   const float dt = load_dt(A, it);
+  const float a_log = load_a_log(A, it);
   OutputOperands<T> oo;
   load_output_operands<T>(A, it, oo);
   __builtin_amdgcn_sched_barrier(0);
@@ -109,7 +110,7 @@ void kda_split_kernel(const Args A, uint32_t* ws) {
   else
     gate_quad_compute<T>(gq, sh);
   __syncthreads();
-  decay<T, false>(A, it, sh, dt);
+  decay<T, false>(A, it, sh, dt, a_log);
   __syncthreads();
 
   // 3. The recurrence on this part's rows (o to the table); the last

@@ -707,10 +707,11 @@ __device__ __forceinline__ void gate_fb_all_compute(const GateFBAll<T>& gf, cons
 // Raw gate to BF16, then the decay of key channel f = tid (threads 0-127);
 // record mode stores raw_g.
 template <int T, bool kRecord, class SH>
-__device__ __forceinline__ void decay(const Args& A, const Item& it, SH& sh, float dt) {
+__device__ __forceinline__ void decay(const Args& A, const Item& it, SH& sh, float dt,
+                                      float a_log) {
   const int tid = threadIdx.x;
   if (tid < kD) {
-    const float e = expf(A.a_log[it.h]);
+    const float e = expf(a_log);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float raw_g = round_bf16(sh.u.in.g[t][tid]);
@@ -747,9 +748,10 @@ __device__ __forceinline__ bool half_step_live(int j) {
 
 // The decay (and the record of raw_g) of decay<T, true>, by token halves.
 template <int T, class SH>
-__device__ __forceinline__ void decay_halves(const Args& A, const Item& it, SH& sh, float dt) {
+__device__ __forceinline__ void decay_halves(const Args& A, const Item& it, SH& sh, float dt,
+                                             float a_log) {
   const int f = threadIdx.x & (kD - 1);
-  const float e = expf(A.a_log[it.h]);
+  const float e = expf(a_log);
 #pragma unroll
   for (int j = 0; j < kHalfTokens<T>; ++j) {
     if (half_step_live<T>(j)) {
@@ -765,6 +767,12 @@ __device__ __forceinline__ void decay_halves(const Args& A, const Item& it, SH& 
 // dt_bias of key channel tid (threads 0-127), loaded with the input operands.
 __device__ __forceinline__ float load_dt(const Args& A, const Item& it) {
   return A.dt_bias[static_cast<size_t>(it.h) * kD + (threadIdx.x & (kD - 1))];
+}
+
+// A_log of the item's head (a scalar load), read in the prologue: a load
+// after a barrier cannot be issued before it, and the decay sits after one.
+__device__ __forceinline__ float load_a_log(const Args& A, const Item& it) {
+  return A.a_log[it.h];
 }
 
 template <int T, class SH>

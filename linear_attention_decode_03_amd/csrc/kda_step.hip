@@ -67,13 +67,14 @@ __device__ __forceinline__ void step_body(const Args& A) {
     gate_quad_load_fb<T>(A, it, gq, 1);
     gate_quad_load_fa<T>(A, it, gq);
   }
-  // Decode at full occupancy has no VGPRs to spare for these two; there they
-  // are loaded where they are used.
+  // Decode at full occupancy has no VGPRs to spare for these two at the
+  // start; there they are loaded after the convolution.
   float beta_logit = 0.0f, dt = 0.0f;
   if constexpr (T > 1 || kLatency) {
     beta_logit = load_beta<T>(A, it);
     dt = load_dt(A, it);
   }
+  const float a_log = load_a_log(A, it);
   OutputOperands<T> oo;
   if constexpr (kLatency) load_output_operands<T>(A, it, oo);
   __builtin_amdgcn_sched_barrier(0);  // not sunk below the slot reads
@@ -101,7 +102,11 @@ __device__ __forceinline__ void step_body(const Args& A) {
 
   // 2. Inputs.
   conv_compute<T, kRecord, kConvF32>(A, it, sh, co);
-  if constexpr (T == 1 && !kLatency) beta_logit = load_beta<T>(A, it);
+  if constexpr (T == 1 && !kLatency) {
+    // Behind the page (loads retire in order), so they arrive with it.
+    beta_logit = load_beta<T>(A, it);
+    dt = load_dt(A, it);
+  }
   store_beta<T>(sh, beta_logit);
   if constexpr (T == 1)
     gate_valu(go, sh);
@@ -113,8 +118,7 @@ __device__ __forceinline__ void step_body(const Args& A) {
     gate_rounds_compute<T>(gr, sh);
   }
   __syncthreads();
-  if constexpr (T == 1 && !kLatency) dt = load_dt(A, it);
-  decay<T, kRecord>(A, it, sh, dt);
+  decay<T, kRecord>(A, it, sh, dt, a_log);
   __syncthreads();
 
   // 3. The recurrence, token by token.
@@ -227,6 +231,7 @@ void kda_record_kernel(const Args A) {
   fa_pairs_load<T>(A, it, fp);
   const float beta_logit = load_beta<T>(A, it);
   const float dt = load_dt(A, it);
+  const float a_log = load_a_log(A, it);
   __builtin_amdgcn_sched_barrier(0);
   SlotRow<T> slot_row;
   if (!resolve<T>(A, it, slot_row)) {
@@ -267,7 +272,7 @@ void kda_record_kernel(const Args A) {
   for (int q = 0; q < 8; ++q) st[1][q] = load_f4(page, voff, 16 * kD * 4 + 64 * q);
   float sink;
   prefetch_page<T>(A, sink);
-  decay_halves<T>(A, it, sh, dt);
+  decay_halves<T>(A, it, sh, dt, a_log);
   __syncthreads();
 
   // 4. W and X (thread = key channel, token half), W zero beyond row 2T.  X
