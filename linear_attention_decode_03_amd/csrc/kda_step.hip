@@ -67,10 +67,14 @@ __device__ __forceinline__ void step_body(const Args& A) {
     gate_quad_load_fb<T>(A, it, gq, 1);
     gate_quad_load_fa<T>(A, it, gq);
   }
-  // Decode at full occupancy has no VGPRs to spare for these two at the
-  // start; there they are loaded after the convolution.
+  // beta and dt ahead of the page, so that nothing before the recurrence
+  // waits for it and the recurrence starts on the first rows of the page
+  // while the rest arrive (loads retire in order).  Decode at full occupancy
+  // with a bias or an FP32 pool has no VGPRs to spare for them at the start
+  // (they would spill); there they are loaded after the convolution.
+  constexpr bool kEarlyScalars = T > 1 || kLatency || (!kBias && !kConvF32);
   float beta_logit = 0.0f, dt = 0.0f;
-  if constexpr (T > 1 || kLatency) {
+  if constexpr (kEarlyScalars) {
     beta_logit = load_beta<T>(A, it);
     dt = load_dt(A, it);
   }
@@ -102,7 +106,7 @@ __device__ __forceinline__ void step_body(const Args& A) {
 
   // 2. Inputs.
   conv_compute<T, kRecord, kConvF32>(A, it, sh, co);
-  if constexpr (T == 1 && !kLatency) {
+  if constexpr (!kEarlyScalars) {
     // Behind the page (loads retire in order), so they arrive with it.
     beta_logit = load_beta<T>(A, it);
     dt = load_dt(A, it);
