@@ -19,7 +19,7 @@ The contract:
 import numpy as np
 
 import oracle
-from linear_attention_decode_03_amd.inputs import from_bf16
+from linear_attention_decode_03_amd.inputs import from_bf16, to_bf16
 
 D = 128
 TIE_BAND = 2.0 ** -18
@@ -28,6 +28,24 @@ TIE_BAND = 2.0 ** -18
 def ulp_bf16(x):
     x = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(x)) - 7)
+
+
+def cancelling_gate_rows(H, D, seed):
+    """F_B rows (H*D of them, D columns, BF16) for a test of the gate's exact
+    sum: each row holds 2^20, 1, 2^-8, 2^-20 and -2^20 at five columns drawn
+    per row, zero elsewhere.  Against f_a = 1 the exact projection is
+    1 + 2^-8 + 2^-20, an FP32 value just above the midpoint between the BF16
+    values 1 and 1 + 2^-7, so the exact sum rounds to 1 + 2^-7.  An FP32 sum
+    that meets 2^20 before the small terms loses them (the FP32 spacing at
+    2^20 is 2^-3) and ends at 1; one that loses only 2^-20 ends on the
+    midpoint, which rounds to even, also 1.  An input generator only: no
+    step of the method is computed here."""
+    rng = np.random.default_rng(seed)
+    fb = np.zeros((H * D, D), np.float32)
+    terms = np.array([2.0 ** 20, 1.0, 2.0 ** -8, 2.0 ** -20, -(2.0 ** 20)], np.float32)
+    for r in range(H * D):
+        fb[r, rng.choice(D, size=5, replace=False)] = terms
+    return to_bf16(fb)
 
 
 def written_targets(p):

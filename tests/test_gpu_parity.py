@@ -406,6 +406,26 @@ def test_gate_modes_agree_gpu(gpu):
         assert np.array_equal(a[k], b[k])
 
 
+@pytest.mark.parametrize("T,record,gate_mode", [(1, 0, 0), (1, 0, 1), (4, 0, 0), (4, 0, 1),
+                                                 (8, 1, 0), (8, 1, 1)])
+def test_gate_sum_exact_on_cancelling_rows_gpu(gpu, T, record, gate_mode):
+    """Kernel body, gate projection: raw_g is the exact sum rounded once to
+    FP32, then to BF16.  With F_B rows 2^20, 1, 2^-8, 2^-20, -2^20 and
+    f_a = 1 every feature's exact raw_g is 1 + 2^-7, while an FP32 running
+    sum ends at 1: the decay then differs by far more than the state
+    tolerance, and in record mode the stored raw_g is compared bit for bit."""
+    cfg = dict(B=4, H=2, T=T, N=4 * T + 3, W=T + 2, seed=811, record=record,
+               gate_mode=gate_mode)
+    p = inputs.make_problem(cfg)
+    p["f_b"] = _parity.cancelling_gate_rows(p["H"], 128, 5)
+    p["f_a"][:] = to_bf16(np.float32(1.0))
+    rep, got, ref = check(gpu, p, f"cancelling gate T={T} record={record} mode={gate_mode}")
+    if record:
+        g = got["rec_kg"][..., 128:].transpose(0, 2, 1, 3)  # [B, T, H, 128]
+        live = np.arange(T)[None, :] < p["accepted"][:, None]
+        assert np.all(g[live] == to_bf16(np.float32(1.0 + 2.0 ** -7)))
+
+
 def test_record_matches_plain_gpu(gpu):
     """Record mode (closed-form kernel) and a plain verify of the same inputs
     both match the oracle; record mode writes no state page, leaves the same

@@ -31,7 +31,7 @@ import pytest
 from linear_attention_decode_03_amd import inputs
 from linear_attention_decode_03_amd.inputs import from_bf16, to_bf16
 
-from . import _matrix_form
+from . import _matrix_form, _parity
 
 D = 128
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -464,6 +464,28 @@ def test_q_scale_applied_after_the_norm_factor(oracle_lib):
     ts = oracle_lib.run(qs, taps=True)
     want = (t1["q_hat"].astype(np.float32) * s).astype(np.float32)
     assert np.array_equal(ts["q_hat"].view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_gate_sum_is_exact_before_rounding(oracle_lib, T):
+    """raw_g = BF16(FP32(exact sum)) (kernel body, gate projection: the FP32
+    accumulation order is free, so the reading takes the exact sum; it is
+    rounded to FP32 once, then to BF16): every feature of the cancelling rows
+    gives 1 + 2^-7, whose decay a test reads through an all-ones state with
+    beta = 0.  An FP32 running sum in column order would give 1 for most."""
+    p = small(T=T, B=2, H=2, seed=97, record=0)
+    if T > 1:
+        p["accepted"][:] = 1
+    p["f_b"] = _parity.cancelling_gate_rows(p["H"], D, 5)
+    p["f_a"][:] = to_bf16(np.float32(1.0))
+    p["beta"][:] = to_bf16(np.full(p["beta"].shape, LOGIT_ZERO, np.float32))
+    p["state"][:] = 1.0
+    taps = oracle_lib.run(p, taps=True)
+    want = np.float32(1.0 + 2.0 ** -7)
+    assert np.all(taps["raw_g"] == want)
+    a = oracle_lib.decay(float(p["a_log"][0]), float(want), float(p["dt_bias"][0]),
+                         p["lower_bound"])
+    assert taps["decay"][0, 0, 0, 0] == np.float32(a)
 
 
 def test_gate_one_hot(oracle_lib):
