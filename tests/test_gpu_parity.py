@@ -124,6 +124,20 @@ def test_record_ragged(gpu, T):
     check(gpu, p, f"record T={T}")
 
 
+@pytest.mark.parametrize("B,H,T", [(45, 32, 5), (250, 5, 3), (40, 48, 8)])
+def test_record_more_items_than_resident(gpu, B, H, T):
+    """More items than record workgroups resident at once (4 per CU, 1024
+    on 256 CUs): the items past the first round run on workgroups started
+    as earlier ones finish; padding in both rounds (items numbered
+    b * H + h)."""
+    p = inputs.make_problem(dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=330 + T, record=1))
+    p["accepted"][3] = 0              # first round
+    p["accepted"][B - 5] = T + 1      # second round
+    p["slots"][B - 2, 0] = -1         # second round: convolution slot out of range
+    p["slots"][B - 1, T - 1] = 0      # an unused entry of the row (record mode writes no page)
+    check(gpu, p, f"record B={B} H={H} T={T}")
+
+
 @pytest.mark.parametrize("B,T", [(3, 1), (5, 1), (3, 4), (5, 8)])
 def test_many_heads(gpu, B, T):
     # H = 128: 16384 channels per row of x, gate and out, 49152 convolution
