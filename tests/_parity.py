@@ -48,6 +48,39 @@ def cancelling_gate_rows(H, D, seed):
     return to_bf16(fb)
 
 
+
+def wide_range_gate_operands(H, D, kind):
+    """F_B rows (H*D of them, all alike) and one f_a row for a test that the
+    gate's products are formed exactly, also beyond FP32's range.  An input
+    generator only: no step of the method is computed here.
+
+    kind "overflow": columns 0 and 1 give the products 2^140 and -2^140
+    (beyond FP32, exact in FP64) and column 2 gives 1 * 0.5, so the exact
+    projection is 0.5; products formed in FP32 overflow to +-inf and sum
+    to NaN.
+
+    kind "tiny": columns 0 and 1 give 2^-120 and 2^-128, whose sum M is the
+    midpoint between the BF16 values 2^-120 and 2^-120 + 2^-127, and the
+    other 126 columns give (1 + 77/128) 2^-151 each (below FP32's smallest
+    subnormal, 2^-149, by a factor 0.4004).  The exact sum is M plus 0.788
+    FP32 ulps at that magnitude (2^-143): it rounds to M + 2^-143 in FP32
+    and up to 2^-120 + 2^-127 in BF16.  Products formed in FP32 round the
+    small ones to 0, leave the midpoint M and round to even, 2^-120."""
+    fb = np.zeros((H * D, D), np.float32)
+    fa = np.zeros(D, np.float32)
+    if kind == "overflow":
+        fb[:, 0], fa[0] = 2.0 ** 70, 2.0 ** 70
+        fb[:, 1], fa[1] = -(2.0 ** 70), 2.0 ** 70
+        fb[:, 2], fa[2] = 1.0, 0.5
+    elif kind == "tiny":
+        fb[:, 0], fa[0] = 2.0 ** -60, 2.0 ** -60
+        fb[:, 1], fa[1] = 2.0 ** -64, 2.0 ** -64
+        fb[:, 2:], fa[2:] = (1.0 + 77.0 / 128.0) * 2.0 ** -76, 2.0 ** -75
+    else:
+        raise ValueError(kind)
+    return to_bf16(fb), to_bf16(fa)
+
+
 def written_targets(p):
     """{slot: [(b, h, t), ...]} of the state pages the step writes."""
     B, H, T = p["B"], p["H"], p["T"]

@@ -440,6 +440,29 @@ def test_gate_sum_exact_on_cancelling_rows_gpu(gpu, T, record, gate_mode):
         assert np.all(g[live] == to_bf16(np.float32(1.0 + 2.0 ** -7)))
 
 
+@pytest.mark.parametrize("T,record,kind", [(1, 0, "overflow"), (4, 0, "overflow"),
+                                            (8, 1, "overflow"), (3, 1, "tiny"), (8, 1, "tiny")])
+def test_gate_products_beyond_fp32_gpu(gpu, T, record, kind):
+    """Kernel body, gate projection: every product exact, also where FP32
+    would overflow (2^140 - 2^140 + 0.5: raw_g 0.5, seen through the
+    decay by the state) or underflow (a sum just off a BF16 midpoint at
+    2^-120, seen in record mode's stored raw_g)."""
+    B, H = 3, 2
+    if T == 1:
+        cfg = dict(B=B, H=H, T=1, N=2 * B + 2, W=3, seed=821)
+    else:
+        cfg = dict(B=B, H=H, T=T, N=B * T + 1, W=T + 2, seed=822 + T, record=record)
+    p = inputs.make_problem(cfg)
+    p["f_b"], fa = _parity.wide_range_gate_operands(H, 128, kind)
+    p["f_a"][:] = fa
+    rep, got, ref = check(gpu, p, f"wide-range gate {kind} T={T} record={record}")
+    if record:
+        want = 0.5 if kind == "overflow" else 2.0 ** -120 + 2.0 ** -127
+        g = got["rec_kg"][..., 128:].transpose(0, 2, 1, 3)  # [B, T, H, 128]
+        live = np.arange(T)[None, :] < p["accepted"][:, None]
+        assert np.all(g[live] == to_bf16(np.float32(want)))
+
+
 def test_record_matches_plain_gpu(gpu):
     """Record mode (closed-form kernel) and a plain verify of the same inputs
     both match the oracle; record mode writes no state page, leaves the same

@@ -59,6 +59,8 @@ MUTANTS = [
     ("gate projection transposed", "g += (double)bf16_to_float(row[j])",
      "g += (double)bf16_to_float(P->f_b[((size_t)h * D + j) * D + f])"),
     ("raw gate not rounded", "raw_g[t][f] = round_bf16((float)g);", "raw_g[t][f] = (float)g;"),
+    ("gate products formed in FP32", "g += (double)bf16_to_float(row[j]) * (double)bf16_to_float(fa[j]);",
+     "g += (double)(bf16_to_float(row[j]) * bf16_to_float(fa[j]));"),
     ("gate summed in FP32", "      double g = 0.0;\n      for (int j = 0; j < D; ++j) g += (double)bf16_to_float(row[j]) * (double)bf16_to_float(fa[j]);",
      "      float g = 0.0f;\n      for (int j = 0; j < D; ++j) g += bf16_to_float(row[j]) * bf16_to_float(fa[j]);"),
     ("decay without exp(A_log)", "float e = (float)exp((double)a_log);", "float e = a_log;"),

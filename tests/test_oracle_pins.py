@@ -488,6 +488,23 @@ def test_gate_sum_is_exact_before_rounding(oracle_lib, T):
     assert taps["decay"][0, 0, 0, 0] == np.float32(a)
 
 
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("kind,want", [("overflow", 0.5), ("tiny", 2.0 ** -120 + 2.0 ** -127)])
+def test_gate_products_exact_beyond_fp32(oracle_lib, T, kind, want):
+    """Each gate product is exact (kernel body, gate projection: products of
+    BF16 values, summed; the reading takes the exact sum): products beyond
+    FP32's range cancel exactly (raw_g = 0.5), and products below its
+    smallest subnormal still move a sum off a BF16 midpoint (raw_g =
+    2^-120 + 2^-127).  Forming the products in FP32 gives NaN and 2^-120."""
+    p = small(T=T, B=2, H=2, seed=98, record=0)
+    if T > 1:
+        p["accepted"][:] = 1
+    p["f_b"], fa = _parity.wide_range_gate_operands(p["H"], D, kind)
+    p["f_a"][:] = fa
+    taps = oracle_lib.run(p, taps=True)
+    assert np.all(taps["raw_g"] == np.float32(want))
+
+
 def test_gate_one_hot(oracle_lib):
     """One-hot F_B rows: raw_g[f] = f_a[pi(f)] bit for bit (record output)."""
     T = 2
