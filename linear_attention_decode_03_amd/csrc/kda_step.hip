@@ -222,9 +222,10 @@ void kda_record_kernel(const Args A) {
   //    page): convolution inputs, all F_B rows of the gate, f_a, beta,
   //    dt_bias before the slot tables are read, the window taps after.  The
   //    page's first row tile is issued right after the taps and arrives
-  //    during the convolution and the gate; the second after the gate,
-  //    behind the output-norm operands.  The scheduling barriers keep the
-  //    groups in this order.
+  //    during the convolution and the gate; the first half of the second
+  //    (keys 0-63) after the convolution, when its operands are dead, and
+  //    the rest after the gate, behind the output-norm operands.  The
+  //    scheduling barriers keep the groups in this order.
   Item it;
   locate<T>(A, it);
   ConvOperands<T> co;
@@ -265,15 +266,17 @@ void kda_record_kernel(const Args A) {
   // 2. Convolution, norms, gate projection.
   conv_compute<T, true, kConvF32>(A, it, sh, co);
   store_beta<T>(sh, beta_logit);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) st[1][q] = load_f4(page, voff, 16 * kD * 4 + 64 * q);
   gate_fb_all_compute<T>(gf, fa64, sh);
   OutputOperands<T> oo;
   load_output_operands<T>(A, it, oo);
   __syncthreads();
 
-  // 3. The page's second row tile; the decay and the W and X tables are
-  //    computed while it arrives.
+  // 3. The rest of the page's second row tile; the decay and the W and X
+  //    tables are computed while it arrives.
 #pragma unroll
-  for (int q = 0; q < 8; ++q) st[1][q] = load_f4(page, voff, 16 * kD * 4 + 64 * q);
+  for (int q = 4; q < 8; ++q) st[1][q] = load_f4(page, voff, 16 * kD * 4 + 64 * q);
   float sink;
   prefetch_page<T>(A, sink);
   decay_halves<T>(A, it, sh, dt, a_log);
