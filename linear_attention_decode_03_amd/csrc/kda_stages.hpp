@@ -355,9 +355,10 @@ __device__ __forceinline__ void conv_compute(const Args& A, const Item& it, SH& 
     }
     if constexpr (kRecord) {
       if (part == 1)
-        *reinterpret_cast<uint32_t*>(
-            &A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + 2 * lane]) =
-            f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+        __builtin_nontemporal_store(
+            f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16),
+            reinterpret_cast<uint32_t*>(
+                &A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + 2 * lane]));
     }
   }
 }
@@ -758,8 +759,9 @@ __device__ __forceinline__ void decay_halves(const Args& A, const Item& it, SH& 
       const int t = half_token<T>(j);
       const float raw_g = round_bf16(sh.u.in.g[t][f]);
       sh.u.in.a[t][f] = decay_f32(e, raw_g, dt, A.lower_bound);
-      A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + kD + f] =
-          static_cast<uint16_t>(f32_to_bf16_bits(raw_g));
+      __builtin_nontemporal_store(
+          static_cast<uint16_t>(f32_to_bf16_bits(raw_g)),
+          &A.rec_kg[((static_cast<size_t>(it.b) * A.H + it.h) * T + t) * (2 * kD) + kD + f]);
     }
   }
 }
