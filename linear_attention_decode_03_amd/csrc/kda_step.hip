@@ -325,14 +325,19 @@ void kda_record_kernel(const Args A) {
   //    every wave has passed a barrier: P overlaps the space of X (the gate
   //    projection's) when T < 6, and wave 0 reads X meanwhile.
   {
-    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f}, cc = {0.f, 0.f, 0.f, 0.f};
+    // Tile 0's products first (two accumulators, alternating q, so that two
+    // independent MFMA chains keep the pipe full), then C on wave 0, then
+    // tile 1's, whose second half is the last of the page to arrive.
+    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0, cc = p0, p0b = p0, p1b = p0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float4 w4 = *reinterpret_cast<const float4*>(&rt.W[c][16 * q + 4 * g]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[0][q], e), p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[1][q], e), p1, 0, 0, 0);
+        if (q & 1)
+          p0b = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[0][q], e), p0b, 0, 0, 0);
+        else
+          p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[0][q], e), p0, 0, 0, 0);
       }
     }
     if (wave == 0) {
@@ -346,6 +351,22 @@ void kda_record_kernel(const Args A) {
         for (int e = 0; e < 4; ++e)
           cc = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(x4, e), cc, 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&rt.W[c][16 * q + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (q & 1)
+          p1b = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[1][q], e), p1b, 0, 0, 0);
+        else
+          p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(w4, e), f4_at(st[1][q], e), p1, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p0[r] += p0b[r];
+      p1[r] += p1b[r];
     }
     __syncthreads();
     // D layout (f32 16x16x4): lane l, element r holds D[4(l/16) + r][l%16].
