@@ -79,7 +79,9 @@ __device__ __forceinline__ float silu_bf16(float x) {
   // Both tests without a branch between them (the fast value is computed
   // for every x; v_exp_f32 and v_rcp_f32 take any argument).
   const bool fast = (ax < 80.0f) & (static_cast<float>(dist) > fmaf(2.0f, ax, 16.0f));
-  if (fast) return round_bf16(yf);
+  // Fast: yf is finite and its low 16 bits are far from 0x8000, so rounding
+  // to nearest is adding half a BF16 ulp and truncating (no tie, no NaN).
+  if (fast) return __uint_as_float((bits + 0x8000u) & 0xffff0000u);
   return silu_bf16_exact(x);
 }
 
