@@ -79,6 +79,10 @@ MUTANTS = [
      "float variance = (float)ss + eps;"),
     ("output gate not a sigmoid", "float sg = sigmoid_f32(bf16_to_float(gate[c]));",
      "float sg = bf16_to_float(gate[c]);"),
+    ("output norm as o * (rstd * nw) * sigma", "float r = ((o_bf[c] * rstd) * bf16_to_float(norm_w[c])) * sg;",
+     "float r = (o_bf[c] * (rstd * bf16_to_float(norm_w[c]))) * sg;"),
+    ("output norm as (o * rstd) * (nw * sigma)", "float r = ((o_bf[c] * rstd) * bf16_to_float(norm_w[c])) * sg;",
+     "float r = (o_bf[c] * rstd) * (bf16_to_float(norm_w[c]) * sg);"),
     ("norm weight of wrong channel", "* bf16_to_float(norm_w[c])) * sg;", "* bf16_to_float(norm_w[0])) * sg;"),
     ("verify reads slot 0 column", "*read_slot = P->slots[(size_t)b * P->slot_stride + *offset];",
      "*read_slot = P->slots[(size_t)b * P->slot_stride];"),

@@ -505,6 +505,25 @@ def test_gate_products_exact_beyond_fp32(oracle_lib, T, kind, want):
     assert np.all(taps["raw_g"] == np.float32(want))
 
 
+def test_output_norm_association(oracle_lib):
+    """out = BF16(((o * rstd) * nw) * sigma(gate)) in that order (kernel body,
+    output norm block).  Hand-built case, derived with exact rational
+    arithmetic and round-to-nearest-even at each FP32 step: all 128 o equal
+    x = 1.7578125 (BF16 0x3fe1) and eps = FP32(1e-6), so Σo² = 128 x² exactly,
+    variance = x² + eps = 3.0899057388305664 and rstd = 0.568888783454895
+    (FP32), x * rstd = 0.9999998211860657.  Channel 0 (nw 0x3f87, gate
+    0xbe42) gives BF16 0x3ef4 and channel 1 (nw 0x3f11, gate 0xbea2) 0x3e74
+    in the page's order; o * (rstd * nw) * σ, (o * rstd) * (nw * σ) and
+    o * ((rstd * nw) * σ) all give 0x3ef5 and 0x3e75."""
+    o = np.full(D, 1.7578125, np.float32)
+    gate = np.zeros(D, np.uint16)
+    nw = np.full(D, 0x3F80, np.uint16)
+    gate[0], nw[0] = 0xBE42, 0x3F87
+    gate[1], nw[1] = 0xBEA2, 0x3F11
+    out = oracle_lib.gated_rmsnorm(o, gate, nw, float(np.float32(1e-6)))
+    assert int(out[0]) == 0x3EF4 and int(out[1]) == 0x3E74
+
+
 def test_gate_one_hot(oracle_lib):
     """One-hot F_B rows: raw_g[f] = f_a[pi(f)] bit for bit (record output)."""
     T = 2
