@@ -134,3 +134,36 @@ def test_split_workspace_reused(gpu, T):
         ref["state"] = got["state"].copy()
         ref["conv_state"] = got["conv_state"].copy()
         ref["out"] = got["out"].copy()
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_split_graph_replays_match_eager(gpu, T):
+    """The split launch allocates nothing and leaves its workspace counters
+    at zero, so it can be captured in a HIP graph: every replay (with the
+    same step launched eagerly on a twin copy, and unrelated work, between
+    replays) gives the eager launch's bits, and the counters stay zero."""
+    import torch
+
+    from linear_attention_decode_03_amd import kda
+
+    p = split_case(4, 32, T, seed=760 + T)
+    eager, graphed = gpu.to_device(copy_problem(p)), gpu.to_device(copy_problem(p))
+    ws_e = kda.split_workspace(p["B"], p["H"], p["T"], eager["state"].device)
+    ws_g = kda.split_workspace(p["B"], p["H"], p["T"], graphed["state"].device)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu.run_split(graphed, ws_g, split=4)
+    torch.cuda.synchronize()
+    for k in range(4):
+        say(f"[split graph] T={T} replay {k}")
+        gpu.run_split(eager, ws_e, split=4)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        scratch = torch.arange(1 << 20, device="cuda", dtype=torch.float32)
+        assert float(scratch.sum()) > 0
+        he, hg = gpu.to_host(eager), gpu.to_host(graphed)
+        for key in ("state", "conv_state", "out"):
+            assert np.array_equal(he[key].view(np.uint8), hg[key].view(np.uint8)), (k, key)
+        assert not ws_g.cpu().numpy()[:p["B"] * p["H"]].any(), k
