@@ -23,7 +23,8 @@
  *   - Every pointer is a DEVICE pointer owned by the caller; BF16 operands are
  *     passed as uint16_t bit patterns.  All tensors are contiguous, row-major,
  *     in the layouts given below.  The library allocates nothing, keeps no
- *     state between calls and never synchronises.
+ *     state between calls (kda_verify_split_noalloc's file-scope device
+ *     array aside) and never synchronises.
  *   - `stream` is a hipStream_t (NULL = the default stream).  The call
  *     validates its arguments on the host, then enqueues one kernel on
  *     `stream` and returns; buffers must stay alive until the stream passes.
