@@ -25,6 +25,10 @@
  *     FP32 as the accumulation type but leaves the order free, and the nearly
  *     exact sum is the value every order approximates;
  *   - BF16 rounding is round-to-nearest-even from FP32.
+ * gate_mode (the constructor's choice between one chain of eight MMAs and
+ * four chains of two for the gate projection) selects an accumulation order
+ * only: both modes take the exact sum here, so neither chained FP32 order is
+ * reproduced -- parity unpinned for that order itself.
  * Built with -O2 -ffp-contract=off so the compiler adds no fused operations:
  * an fma appears only where the page writes one.
  *
