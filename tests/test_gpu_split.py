@@ -167,3 +167,34 @@ def test_split_graph_replays_match_eager(gpu, T):
         for key in ("state", "conv_state", "out"):
             assert np.array_equal(he[key].view(np.uint8), hg[key].view(np.uint8)), (k, key)
         assert not ws_g.cpu().numpy()[:p["B"] * p["H"]].any(), k
+
+
+def test_split_concurrent_streams_own_workspaces(gpu):
+    """Two split launches on two streams, each with its own workspace, may run
+    at the same time: each gives the unsplit kernel's bits and leaves its
+    counters at zero."""
+    import torch
+
+    from linear_attention_decode_03_amd import kda
+
+    probs = [split_case(4, 32, 4, seed=780), split_case(2, 32, 1, seed=781)]
+    devs = [gpu.to_device(p) for p in probs]
+    wss = [kda.split_workspace(p["B"], p["H"], p["T"], d["state"].device)
+           for p, d in zip(probs, devs)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for d, ws, s in zip(devs, wss, streams):
+            with torch.cuda.stream(s):
+                gpu.run_split(d, ws, split=4, stream=s)
+    torch.cuda.synchronize()
+    for k, (p, d, ws) in enumerate(zip(probs, devs, wss)):
+        plain = gpu.to_device(p)
+        for _ in range(3):
+            gpu.run(plain)
+        torch.cuda.synchronize()
+        got, want = gpu.to_host(d), gpu.to_host(plain)
+        say(f"[split streams] problem {k}: T={p['T']}")
+        for key in ("state", "conv_state", "out"):
+            assert np.array_equal(got[key].view(np.uint8), want[key].view(np.uint8)), (k, key)
+        assert not ws.cpu().numpy()[:p["B"] * p["H"]].any(), k
