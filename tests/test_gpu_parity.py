@@ -138,19 +138,22 @@ def test_record_more_items_than_resident(gpu, B, H, T):
     check(gpu, p, f"record B={B} H={H} T={T}")
 
 
-@pytest.mark.parametrize("B,T", [(3, 1), (5, 1), (3, 4), (5, 8)])
-def test_many_heads(gpu, B, T):
+@pytest.mark.parametrize("B,T,record", [(3, 1, 0), (5, 1, 0), (3, 4, 0), (5, 8, 0), (5, 8, 1),
+                                         (3, 3, 1)])
+def test_many_heads(gpu, B, T, record):
     # H = 128: 16384 channels per row of x, gate and out, 49152 convolution
     # channels; 384 items run the latency kernel, 640 the full-occupancy one
+    # (record mode: the closed-form kernel at either size)
     H = 128
-    cfg = dict(B=B, H=H, T=T, N=B * T + 2, W=T + 2 if T > 1 else 3, seed=700 + B + T)
+    cfg = dict(B=B, H=H, T=T, N=B * T + 2, W=T + 2 if T > 1 else 3, seed=700 + B + T,
+               record=record)
     p = inputs.make_problem(cfg)
     if B > 3:
         if T == 1:
             p["slots"][1] = 0
         else:
             p["accepted"][1] = 0
-    check(gpu, p, f"many heads B={B} T={T}")
+    check(gpu, p, f"many heads B={B} T={T} record={record}")
 
 
 @pytest.mark.parametrize("T,record", [(1, 0), (4, 0), (8, 1)])
