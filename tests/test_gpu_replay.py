@@ -43,7 +43,9 @@ def replay_gpu(gpu, r):
 
 
 @pytest.mark.parametrize("cfg", ["replay_t8", dict(B=5, H=3, T=3, N=13, seed=21),
-                                 dict(B=7, H=2, T=8, N=17, seed=22, lower_bound=-12.0)])
+                                 dict(B=7, H=2, T=8, N=17, seed=22, lower_bound=-12.0),
+                                 dict(B=4, H=128, T=6, N=11, seed=24),
+                                 dict(B=3, H=1, T=1, N=7, seed=25)])
 def test_replay_parity(gpu, cfg):
     r = inputs.make_replay_problem(cfg)
     if not isinstance(cfg, str):
